@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-KV decode step on one MI355X.
+
+A step is one pass of the whole hot path -- landmark scoring, per-KV-head
+top-k, the paged gather fused into the attention loads, split-K attention over
+the selected blocks plus the recent window, and the log-sum-exp merge -- over
+one batch of seeded synthetic inputs already resident in HBM.  Steps rotate
+over several independent input instances so that neither the landmarks nor
+the K/V blocks can be served from the 256 MB last-level cache between steps.
+
+Prints one JSON line: tokens/s (real query tokens per second), the dominant
+kernel's roofline (attention, algorithmic HBM bytes per launch over its mean
+launch time from HIP events on the launch stream), and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_bytes(wl, seq_lens, nsel_real) -> int:
+    """Algorithmic bytes of one attention launch: the selected K/V chunks (and
+    fp8 scales), the window's K/V, the real-token queries, the fp32 output and
+    lse."""
+    from sparse_kv_cache_block_amd.configs import ELEM_BYTES
+    d, blk = wl.head_dim, wl.block_size
+    e_kv = ELEM_BYTES[wl.kv_dtype]
+    e_scale = 8 if wl.kv_dtype == "fp8" else 0
+    total = int(nsel_real.sum()) * (2 * blk * d * e_kv + e_scale)
+    for L in seq_lens:
+        total += wl.n_kv_heads * min(wl.window, int(L)) * 2 * d * e_kv
+    total += wl.batch * wl.n_q_heads * d * ELEM_BYTES[wl.q_dtype]
+    total += wl.batch * wl.n_q_heads * (d + 1) * 4
+    return total
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama32k",
+                    help="llama32k (default), ragged, host, dual or tiny")
+    ap.add_argument("--instances", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 disables it)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs the single-GPU decode step only; --gpus {args.gpus} "
+              f"(WORLD_SIZE {world}) is not supported: each (sequence, KV head) pair is "
+              "independent, so more GPUs would each run this same kernel on their own share.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_kv_cache_block_amd import binding as B
+    from sparse_kv_cache_block_amd import configs
+    from sparse_kv_cache_block_amd.inputs import make_inputs
+    from sparse_kv_cache_block_amd.step import DecodeStep, to_device_for
+
+    wl = configs.get(args.workload)
+    torch.cuda.set_device(0)
+    B.lib()
+
+    # ---- inputs: independent instances generated on the GPU
+    steps = []
+    host_inputs = None
+    for i in range(args.instances):
+        t0 = time.perf_counter()
+        inp = make_inputs(wl, device="cuda", instance=i)
+        if i == 0 and args.cpu_budget > 0:
+            host_inputs = inp.to("cpu")
+        if wl.pool == "host":
+            inp = to_device_for(inp)   # the K/V pool moves to pinned host memory
+        st = DecodeStep(inp)
+        steps.append(st)
+        torch.cuda.synchronize()
+        log(f"instance {i} ready in {time.perf_counter() - t0:.1f}s")
+
+    n_layers = wl.n_layers if wl.pool == "host" else 1
+    copy_stream = torch.cuda.Stream() if wl.pool == "host" else None
+
+    def one_step(k: int) -> None:
+        st = steps[k % len(steps)]
+        if wl.pool == "host":
+            st.run_layers(n_layers, copy_stream=copy_stream)
+        else:
+            st.run()
+
+    for k in range(args.warmup):
+        one_step(k)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for k in range(args.steps):
+        one_step(k)
+    ev1.record(stream)
+    ev1.synchronize()
+    wall1 = time.perf_counter()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    wall_ms = (wall1 - wall0) * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us)")
+
+    lens = steps[0].inp.seq_lens.cpu().numpy()
+    kps = steps[0].inp.k_per_seq.cpu().numpy()
+    step_bytes = configs.algorithmic_bytes(wl, lens, kps)
+    tokens_per_s = wl.batch * n_layers / (ms_per_step * 1e-3)
+
+    # ---- dominant kernel: the attention launch, timed alone over the same instances
+    attn_ms = None
+    attn_bytes = None
+    if wl.pool != "host":
+        launches = []
+        for st in steps:
+            d = st.inp
+            sparse = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
+            launches.append((st, sparse))
+        for k in range(args.warmup):
+            st, sp = launches[k % len(launches)]
+            B.sparsekv_attend(st.pr, st.inp.q, sp, st.indices, st.n_sel, sp, st.inp.seq_lens,
+                              st.out, st.lse, st.ws)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for k in range(args.steps):
+            st, sp = launches[k % len(launches)]
+            B.sparsekv_attend(st.pr, st.inp.q, sp, st.indices, st.n_sel, sp, st.inp.seq_lens,
+                              st.out, st.lse, st.ws)
+        ev1.record(stream)
+        ev1.synchronize()
+        attn_ms = ev0.elapsed_time(ev1) / args.steps
+        per_inst = [attention_bytes(wl, s.inp.seq_lens.cpu().numpy(), s.n_sel[:, 0].cpu().numpy())
+                    for s in steps]
+        attn_bytes = statistics.mean(per_inst)
+        log(f"attention kernel alone: {attn_ms * 1e3:.1f} us, {attn_bytes / 1e6:.1f} MB")
+
+    roofline = None
+    if attn_ms:
+        achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "attend_kernel", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": None, "bytes_per_launch": int(attn_bytes),
+                    "us_per_launch": round(attn_ms * 1e3, 2)}
+
+    # ---- CPU oracle on a bounded sample of instance 0
+    cpu = None
+    if args.cpu_budget > 0 and host_inputs is not None:
+        from oracle import oracle as O
+        from tests.common import HostArrays, oracle_problem
+        h = HostArrays(host_inputs)
+        pr = oracle_problem(host_inputs)
+        log("timing the CPU oracle")
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
+            times.append(time.perf_counter() - t0)
+            spent = time.perf_counter() - t_start
+            if len(times) >= 50 or (len(times) >= 3 and spent > args.cpu_budget):
+                break
+        t = statistics.median(times)
+        cpu = {"value": round(wl.batch / t, 2), "unit": "tokens/s", "cores": O.max_threads(),
+               "kind": "oracle",
+               "sample": f"{len(times)} full {wl.name} decode steps (B={wl.batch}) on instance 0, "
+                         f"fp64, median {t:.2f}s",
+               "gbps": round(step_bytes / t / 1e9, 3)}
+
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    cfg = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "n_q_heads": wl.n_q_heads,
+           "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+           "top_k": wl.top_k, "window": wl.window, "kv_dtype": wl.kv_dtype,
+           "n_q_tokens": wl.n_q_tokens, "pool": wl.pool, "instances": args.instances}
+    if n_layers > 1:
+        cfg["layers_per_step"] = n_layers
+    line = {
+        "metric": "sparse decode steps: tokens/s and achieved HBM GB/s (% roofline) at 32k context",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp32": "f32", "bf16": "bf16", "fp8": "fp8e4m3"}[wl.kv_dtype],
+        "data": "synthetic",
+        "config": cfg,
+        "step_bytes": int(step_bytes),
+        "step_gbps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBS, 4),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if wl.n_q_tokens == 2:
+        line["overlap_mean"] = round(float(steps[0].overlap.mean().item()), 4)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,236 @@
+/*
+ * sparsekv.h -- C ABI of the MI355X (gfx950) sparse-KV decode step.
+ *
+ * One decode step of one attention layer over a paged KV cache:
+ *   score    every historical block's landmark against the query
+ *            (DualDecoder review, core claim and axiom ledger item 1: the
+ *            retrieval index follows from the query and landmarks resident on
+ *            the GPU; the landmark is the mean of the block's keys);
+ *   top-k    per KV head, keep the k highest-scoring blocks (PulseInfer
+ *            article, section 2: per-head sparse selection; DualDecoder
+ *            ledger: a sparse KV budget);
+ *   gather   copy the selected (block, head) chunks into a dense staging
+ *            buffer (PulseInfer section 2: gather-scatter I/O engine that
+ *            coalesces fragmented transfers; DualDecoder Fig. 19: contiguous
+ *            block fetch plus a GPU reorder; Fig. 11: two-layer ping-pong
+ *            staging buffer);
+ *   attend   split-K attention over the selected blocks plus dense attention
+ *            over the recent window, the partial results fused by
+ *            log-sum-exp (Beyond abstract).
+ *
+ * Notation: B batch, T query tokens per sequence (1, or 2 = real +
+ * speculative), Hq query heads, Hkv KV heads, G = Hq/Hkv, d head dim, blk
+ * block size in tokens, L_b length of sequence b, W window, ws_b =
+ * max(0, L_b - W) window start.  Candidate blocks of sequence b are
+ * j in [0, ceil(ws_b/blk)) (blocks holding a position before the window).
+ *
+ * Layouts (row-major, innermost last; "elements" are of the stated dtype):
+ *   q          [B][T][Hq][d]            q_dtype
+ *   landmarks  [B][Hkv][max_blocks][d]  landmark_dtype, logical block order
+ *   K/V pool   chunk (p, g) = [blk][d] contiguous at element offset
+ *              p*pool_stride_block + g*pool_stride_head  (kv_dtype)
+ *   k/v scales [P][Hkv] fp32, fp8 pools only: value = code * scale
+ *   block_table[B][max_blocks] int32 physical block of logical block j
+ *   seq_lens   [B] int32,  k_per_seq [B] int32
+ *   scores     [B][T][Hkv][max_blocks] fp32 (-inf for non-candidates)
+ *   indices    [B][T][Hkv][k_max] int32, ascending block ids, -1 padded
+ *   n_sel      [B][T][Hkv] int32 = min(k_b, #candidates)
+ *   stage      [B][Hkv][k_max][blk][d] kv_dtype; stage scales [B][Hkv][k_max]
+ *   window buf [B][Hkv][W][d] kv_dtype: row r holds position ws_b + r
+ *   out        [B][Hq][d] fp32 (real token), lse [B][Hq] fp32 (natural log)
+ *   overlap    [B][Hkv] fp32 = |I_real & I_spec| / |I_real| (T == 2)
+ *
+ * Ownership and execution: the caller owns every buffer (device memory, or
+ * pinned host memory for a host pool).  The library never allocates, frees or
+ * synchronises; all work is enqueued on the given HIP stream (NULL = default
+ * stream) and is asynchronous.  Keep buffers alive until it completes.
+ *
+ * Errors: every argument is checked on the host before any launch; a bad
+ * argument returns a non-zero status and launches nothing.  Unsupported
+ * combinations return SKV_E_UNSUPPORTED (never a silent fallback).  A failed
+ * launch returns SKV_E_HIP with the runtime's text in sparsekv_last_error().
+ * Device-resident values (block ids, lengths, k) are not checked: an
+ * out-of-range block id or a length above max_blocks*blk is undefined
+ * behaviour.  No C++ exception crosses this interface.
+ *
+ * Supported: d in {64, 128}; blk in {16, 32, 64}; 1 <= G <= 8; T in {1, 2};
+ * kv fp32 with q fp32, or kv bf16 / fp8 e4m3fn with q bf16; landmarks fp32 or
+ * bf16; max_blocks <= 16384; k_max <= max_blocks.
+ */
+#ifndef SPARSEKV_H
+#define SPARSEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SKV_OK = 0,
+    SKV_E_NULL = 1,         /* a required pointer is NULL */
+    SKV_E_SHAPE = 2,        /* a size is non-positive or inconsistent */
+    SKV_E_DTYPE = 3,        /* unknown dtype code */
+    SKV_E_UNSUPPORTED = 4,  /* valid but not implemented combination */
+    SKV_E_WORKSPACE = 5,    /* workspace missing or too small */
+    SKV_E_HIP = 6           /* the HIP runtime reported an error */
+} skv_status;
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1, SKV_FP8_E4M3FN = 2 } skv_dtype;
+typedef enum { SKV_POOL_DEVICE = 0, SKV_POOL_HOST = 1 } skv_pool_location;
+
+/* One layer, one decode step. */
+typedef struct {
+    int32_t batch;               /* B >= 1 */
+    int32_t n_q_tokens;          /* T: 1, or 2 (real, speculative) */
+    int32_t n_q_heads;           /* Hq, a multiple of n_kv_heads */
+    int32_t n_kv_heads;          /* Hkv */
+    int32_t head_dim;            /* d */
+    int32_t block_size;          /* blk */
+    int32_t max_blocks_per_seq;  /* columns of block_table and landmarks */
+    int32_t n_pool_blocks;       /* P */
+    int64_t pool_stride_block;   /* elements between pool blocks p and p+1 */
+    int64_t pool_stride_head;    /* elements between heads g and g+1 of a block */
+    int32_t window;              /* W >= 0 */
+    int32_t k_max;               /* >= every k_b; columns of indices */
+    int32_t q_dtype, kv_dtype, landmark_dtype;  /* skv_dtype */
+    int32_t pool_location;       /* skv_pool_location */
+} skv_problem;
+
+/* Where attention reads K/V from. */
+typedef enum {
+    SKV_SRC_PAGED = 0,   /* pool chunks through block_table (and indices for the sparse part) */
+    SKV_SRC_STAGED = 1,  /* gathered stage buffers, slot m = m-th selected block */
+    SKV_SRC_WINDOW = 2   /* window buffers [B][Hkv][W][d]; needs W % blk == 0; not fp8 */
+} skv_source_kind;
+
+typedef struct {
+    int32_t kind;                /* skv_source_kind */
+    const void *k, *v;           /* pool, stage or window buffers */
+    const float *k_scales, *v_scales;  /* fp8: pool [P][Hkv] or stage [B][Hkv][k_max] */
+    const int32_t *block_table;  /* PAGED only */
+} skv_kv_source;
+
+/* Per-layer inputs of a full decode step. */
+typedef struct {
+    const void *q, *landmarks;
+    const void *k_pool, *v_pool;
+    const float *k_scales, *v_scales;  /* fp8 only */
+    const int32_t *block_table, *seq_lens, *k_per_seq;
+    const void *window_k, *window_v;   /* host pools: HBM window buffers; else NULL */
+} skv_step_inputs;
+
+/* Per-layer outputs of a full decode step. */
+typedef struct {
+    int32_t *indices, *n_sel;
+    float *out, *lse;            /* lse may be NULL */
+    float *overlap;              /* T == 2 only; may be NULL */
+} skv_step_outputs;
+
+const char *sparsekv_status_string(int status);
+/* Text of the last SKV_E_HIP / validation failure on the calling thread. */
+const char *sparsekv_last_error(void);
+/* Library version as "major.minor.patch". */
+const char *sparsekv_version(void);
+
+/*
+ * Workspace: device scratch for split partials, score staging and arrival
+ * counters.  sparsekv_workspace_size() gives the bytes needed by
+ * sparsekv_attend / sparsekv_decode_step / sparsekv_decode_layers for a
+ * problem.  A new workspace must be cleared once with sparsekv_workspace_init
+ * (a fill kernel, safe inside graph capture); every call returns its counters
+ * to zero when it completes, so no further clearing is needed.  Calls that
+ * share a workspace must not overlap in time.
+ */
+skv_status sparsekv_workspace_size(const skv_problem *pr, size_t *bytes);
+skv_status sparsekv_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/*
+ * Landmark scoring (score step above).  For t < T, g < Hkv and candidate j:
+ *   scores[b,t,g,j] = sum_{h = gG}^{gG+G-1} q[b,t,h,:] . landmarks[b,g,j,:]
+ * accumulated in fp32 (no 1/sqrt(d): ranking only); -inf for j beyond the
+ * candidates.  One landmark load serves every query token.
+ */
+skv_status sparsekv_score(const skv_problem *pr, const void *q, const void *landmarks,
+                          const int32_t *seq_lens, float *scores, void *stream);
+
+/*
+ * Per-KV-head top-k (top-k step above): k'_b = min(k_per_seq[b], #candidates)
+ * blocks with the largest score, ties to the lowest block id, written in
+ * ascending id order and padded with -1; n_sel = k'_b.  With T == 2 and a
+ * non-NULL overlap, also writes the index-overlap fraction of the two tokens
+ * (DualDecoder review: retrieval-index prediction accuracy; 1.0 when k' = 0).
+ */
+skv_status sparsekv_topk(const skv_problem *pr, const float *scores, const int32_t *seq_lens,
+                         const int32_t *k_per_seq, int32_t *indices, int32_t *n_sel,
+                         float *overlap, void *stream);
+
+/*
+ * Gather (gather step above): for the real token's selection, copy each
+ * selected (block, head) chunk of K and V -- and, for fp8, its two scales --
+ * into staging slot m, byte for byte.  Slots >= n_sel are left untouched.
+ * k_pool / v_pool may be pinned host memory (pool_location HOST): the copy
+ * then reads it over the host link with 16-byte loads.
+ */
+skv_status sparsekv_gather(const skv_problem *pr, const void *k_pool, const void *v_pool,
+                           const float *k_scales, const float *v_scales,
+                           const int32_t *block_table, const int32_t *indices,
+                           const int32_t *n_sel, void *k_stage, void *v_stage,
+                           float *k_stage_scales, float *v_stage_scales, void *stream);
+
+/*
+ * Attention (attend step above) for the real token (t = 0) of every query
+ * head h of group g:
+ *   sparse part: positions p = j*blk + r of the selected blocks j with p < ws_b
+ *   window part: positions [ws_b, L_b)
+ *   z_p = q_h . k_p / sqrt(d); each part is split over workgroups (split-K)
+ *   and every split's (max, sum, unnormalised output) is fused by
+ *   log-sum-exp into out (fp32) and lse = ln sum_p e^{z_p}.
+ * Empty parts contribute nothing; with no position at all, out = 0 and
+ * lse = -inf.  sparse->kind is PAGED (indices index the block table) or
+ * STAGED; window->kind is PAGED or WINDOW.
+ */
+skv_status sparsekv_attend(const skv_problem *pr, const void *q, const skv_kv_source *sparse,
+                           const int32_t *indices, const int32_t *n_sel,
+                           const skv_kv_source *window, const int32_t *seq_lens,
+                           float *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * Full decode step.  Device pool: scoring with in-kernel top-k, then
+ * attention straight from the paged pool (the gather is fused into the
+ * attention's loads; nothing is staged).  Host pool: scoring and top-k on
+ * `stream`, the gather from pinned host memory into k_stage/v_stage on
+ * `copy_stream` (ordered by events), then attention of the staged blocks plus
+ * the HBM window buffers on `stream`.  k_stage/v_stage ([B][Hkv][k_max][blk][d])
+ * are required for host pools and ignored otherwise; copy_stream may be NULL
+ * (then `stream` is used).
+ */
+skv_status sparsekv_decode_step(const skv_problem *pr, const skv_step_inputs *in,
+                                const skv_step_outputs *out, void *k_stage, void *v_stage,
+                                float *k_stage_scales, float *v_stage_scales,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream, void *copy_stream);
+
+/*
+ * Host-pool layer pipeline with a two-slot (ping-pong) staging buffer
+ * (DualDecoder Fig. 11 and the layer-aware schedule of its mechanism
+ * summary).  Layer l's blocks are gathered into slot l % 2 on copy_stream as
+ * soon as its indices exist and layer l-2's attention has released the slot;
+ * attention of layer l runs on stream once its gather is done.  The staging
+ * footprint is two slots for any number of layers.  in[l] / out[l] are the
+ * per-layer inputs and outputs (n_layers >= 1); k_stage[2] / v_stage[2] are
+ * the two slots.
+ */
+skv_status sparsekv_decode_layers(const skv_problem *pr, int32_t n_layers,
+                                  const skv_step_inputs *in, const skv_step_outputs *out,
+                                  void *const *k_stage, void *const *v_stage,
+                                  float *const *k_stage_scales, float *const *v_stage_scales,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream, void *copy_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSEKV_H */

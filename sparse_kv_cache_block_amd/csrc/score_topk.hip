@@ -1,0 +1,346 @@
+// score_topk.hip -- landmark scoring and per-KV-head top-k block selection
+// for gfx950.
+//
+// Scoring (DualDecoder review, core claim and axiom ledger item 1: the
+// retrieval index follows from the query and the landmarks resident on the
+// GPU): score(b,t,g,j) = qbar(b,t,g) . landmark(b,g,j), where qbar is the sum
+// of the G query heads of KV head g.  Summing the heads first turns the
+// group's G dot products into one, so the kernel is a streaming gemv over the
+// landmarks: each landmark row is read once with 16-byte loads (16 lanes per
+// 256-byte bf16 row) and serves both query tokens of a dual-query step.
+//
+// Selection (PulseInfer article, section 2: per-head sparse selection;
+// DualDecoder ledger: a budget of k blocks): a 256-thread LDS radix select on
+// order-preserving 32-bit keys (four 8-bit passes) finds the k-th largest key;
+// blocks above it are kept, blocks equal to it are kept in ascending id order
+// until k are chosen (ties to the lowest id), and the chosen ids are written
+// in ascending order after one block-wide scan.
+//
+// In the fused decode step the scoring grid is split over workgroups per
+// (sequence, KV head); the last workgroup to finish (device-scope atomic
+// counter, reset by that workgroup) runs the selection over the fp32 scores
+// its siblings left in the workspace.
+#include "skv_device.h"
+#include "skv_internal.h"
+
+namespace skv {
+
+// ------------------------------------------------------------ block scan
+
+// Exclusive prefix sum over the 256 threads of a workgroup.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds4, uint32_t& total) {
+  const int lane = lane_id(), w = wave_id();
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) lds4[w] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    uint32_t t = lds4[i];
+    base += (i < w) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+struct TopkShared {
+  uint32_t hist[256];
+  uint32_t scan4[kWaves];
+  uint32_t digit, above, common;
+};
+
+// Select the k largest of keys[0..n) (ties to the lowest index).  Writes the
+// chosen indices in ascending order to out[0..k') and -1 to out[k'..k_max);
+// mirrors them to lds_out when given.  Returns k' = clamp(k, 0, min(n, k_max)).
+__device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32_t* out,
+                            int32_t* lds_out, TopkShared& sh) {
+  const int tid = threadIdx.x;
+  int kk = k < n ? k : n;
+  if (kk > k_max) kk = k_max;  // the output row holds k_max entries
+  if (kk < 0) kk = 0;
+  const bool take_all = kk >= n;
+  uint32_t thresh = 0, take_eq = 0;
+  if (!take_all && kk > 0) {
+    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kk;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      sh.hist[tid] = 0;
+      __syncthreads();
+      for (int j = tid; j < n; j += kThreads) {
+        const uint32_t key = keys[j];
+        if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      // thread tid owns digit 255 - tid: the scan gives how many keys lie above it
+      const uint32_t c = sh.hist[255 - tid];
+      uint32_t tot;
+      const uint32_t above = block_exclusive_scan(c, sh.scan4, tot);
+      if (above < remaining && above + c >= remaining) {
+        sh.digit = 255u - tid;
+        sh.above = above;
+      }
+      __syncthreads();
+      prefix |= sh.digit << shift;
+      pmask |= 255u << shift;
+      remaining -= sh.above;
+      __syncthreads();
+    }
+    thresh = prefix;
+    take_eq = remaining;
+  }
+  // Emit in ascending index order: thread tid owns indices [j0, j1).
+  const int per = (n + kThreads - 1) / kThreads;
+  const int j0 = tid * per;
+  const int j1 = min(n, j0 + per);
+  uint32_t gt = 0, eq = 0;
+  if (!take_all && kk > 0)
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = keys[j];
+      gt += key > thresh;
+      eq += key == thresh;
+    }
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.scan4, tot);
+  if (take_all) {
+    for (int j = j0; j < j1; ++j) {
+      out[j] = j;
+      if (lds_out) lds_out[j] = j;
+    }
+  } else if (kk > 0) {
+    const uint32_t gt_before = ex >> 16, eq_before = ex & 0xffffu;
+    int pos = (int)(gt_before + min(eq_before, take_eq));
+    uint32_t eq_seen = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = keys[j];
+      bool keep = key > thresh;
+      if (key == thresh) {
+        keep = eq_seen < take_eq;
+        ++eq_seen;
+      }
+      if (keep) {
+        out[pos] = j;
+        if (lds_out) lds_out[pos] = j;
+        ++pos;
+      }
+    }
+  }
+  const int nsel = take_all ? n : kk;
+  for (int m = nsel + tid; m < k_max; m += kThreads) {
+    out[m] = -1;
+    if (lds_out) lds_out[m] = -1;
+  }
+  return nsel;
+}
+
+// |a & b| / |a| for two ascending index lists in LDS (1 when a is empty).
+__device__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb, TopkShared& sh) {
+  if (threadIdx.x == 0) sh.common = 0;
+  __syncthreads();
+  uint32_t local = 0;
+  for (int i = threadIdx.x; i < na; i += kThreads) {
+    const int x = a[i];
+    int lo = 0, hi = nb;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (b[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    local += (lo < nb && b[lo] == x) ? 1u : 0u;
+  }
+  if (local) atomicAdd(&sh.common, local);
+  __syncthreads();
+  return na > 0 ? (float)sh.common / (float)na : 1.0f;
+}
+
+__device__ __forceinline__ int n_candidates(int L, int window, int blk) {
+  const int ws = L - window > 0 ? L - window : 0;
+  return (ws + blk - 1) / blk;
+}
+
+// Selection for one (b, g) and every query token, keys read from `scores`
+// (row stride `cols`).  Dynamic LDS layout: keys[max_cand] | idx[2][k_max].
+__device__ void select_rows(const float* scores, int64_t t_stride, int nc, int T, int k, int k_max,
+                            int32_t* indices, int64_t idx_t_stride, int32_t* n_sel,
+                            int64_t nsel_t_stride, float* overlap_out, uint32_t* keys,
+                            int32_t* lds_idx, TopkShared& sh) {
+  int ns[2] = {0, 0};
+  for (int t = 0; t < T; ++t) {
+    const float* row = scores + t * t_stride;
+    for (int j = threadIdx.x; j < nc; j += kThreads) keys[j] = score_key(row[j]);
+    __syncthreads();
+    ns[t] = block_select(keys, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
+    if (threadIdx.x == 0) n_sel[t * nsel_t_stride] = ns[t];
+    __syncthreads();
+  }
+  if (T == 2 && overlap_out) {
+    const float ov = list_overlap(lds_idx, ns[0], lds_idx + k_max, ns[1], sh);
+    if (threadIdx.x == 0) *overlap_out = ov;
+  }
+}
+
+// ------------------------------------------------------------ scoring
+
+template <int D, bool LM_F32>
+__global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
+  constexpr int ES = LM_F32 ? 4 : 2;
+  constexpr int LPR = D * ES / 16;   // lanes per landmark row
+  constexpr int EPL = 16 / ES;       // landmark elements per lane
+  constexpr int RPW = kWave / LPR;   // rows per wave per step
+  constexpr int RPS = RPW * kWaves;  // rows per workgroup per step
+  constexpr int UR = 4;              // steps whose loads are in flight together
+
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int T = p.T;
+  const int L = p.seq_lens[b];
+  const int nc = n_candidates(L, p.window, p.blk);
+  const int R = p.rows_per_chunk;
+  int row_begin, row_end, nchunks = 1;
+  if (p.fused_select) {
+    nchunks = max(1, (nc + R - 1) / R);
+    if (c >= nchunks) return;
+    row_begin = c * R;
+    row_end = min(nc, row_begin + R);
+  } else {
+    row_begin = c * R;
+    row_end = min(p.max_blocks, row_begin + R);
+  }
+
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  float* qbar = reinterpret_cast<float*>(smem);  // [T][D]
+  for (int i = threadIdx.x; i < T * D; i += kThreads) {
+    const int t = i / D, d = i % D;
+    const int64_t base = ((int64_t)(b * T + t) * p.Hq + (int64_t)g * p.G) * D + d;
+    float s = 0.f;
+    for (int h = 0; h < p.G; ++h)
+      s += p.q_f32 ? static_cast<const float*>(p.q)[base + (int64_t)h * D]
+                   : bf16_to_f32(static_cast<const uint16_t*>(p.q)[base + (int64_t)h * D]);
+    qbar[i] = s;
+  }
+  __syncthreads();
+
+  const int lane = lane_id(), w = wave_id();
+  const int sub = lane % LPR, rw = lane / LPR;
+  float qr[2][EPL];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qr[t][e] = (t < T) ? qbar[t * D + sub * EPL + e] : 0.f;
+
+  const char* lm = static_cast<const char*>(p.landmarks) +
+                   ((int64_t)(b * p.Hkv + g) * p.max_blocks) * D * ES + sub * 16;
+  float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
+  const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
+
+  const int steps = (row_end - row_begin + RPS - 1) / RPS;
+  for (int s0 = 0; s0 < steps; s0 += UR) {
+    uint4 v[UR];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
+      v[u] = (s0 + u < steps && r < row_end && r < nc)
+                 ? *reinterpret_cast<const uint4*>(lm + (int64_t)r * D * ES)
+                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
+      float x[EPL];
+      if constexpr (LM_F32) {
+        x[0] = __uint_as_float(v[u].x); x[1] = __uint_as_float(v[u].y);
+        x[2] = __uint_as_float(v[u].z); x[3] = __uint_as_float(v[u].w);
+      } else {
+        x[0] = bf16_lo(v[u].x); x[1] = bf16_hi(v[u].x); x[2] = bf16_lo(v[u].y); x[3] = bf16_hi(v[u].y);
+        x[4] = bf16_lo(v[u].z); x[5] = bf16_hi(v[u].z); x[6] = bf16_lo(v[u].w); x[7] = bf16_hi(v[u].w);
+      }
+      float acc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(qr[t][e], x[e], a);
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) a += shfl_xor_f(a, off);
+        acc[t] = a;
+      }
+      if (sub == 0 && s0 + u < steps && r < row_end) {
+        for (int t = 0; t < T; ++t) {
+          float val = acc[t];
+          if (val == 0.0f) val = 0.0f;  // one zero
+          sc[t * t_stride + r] = (r < nc) ? val : -INFINITY;
+        }
+      }
+    }
+  }
+
+  if (!p.fused_select) return;
+
+  // ---- last workgroup of (b, g) selects
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned* cnt = p.counters + b * p.Hkv + g;
+    const unsigned old = atomicAdd(cnt, 1u);
+    s_last = (old == (unsigned)(nchunks - 1));
+    if (s_last) *cnt = 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  __shared__ TopkShared sh;
+  uint32_t* keys = smem + T * D;
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + p.score_cols);
+  const int k = p.k_per_seq[b];
+  select_rows(sc, t_stride, nc, T, k, p.k_max,
+              p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max,
+              p.n_sel + (int64_t)b * T * p.Hkv + g, p.Hkv,
+              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh);
+}
+
+// Stand-alone selection over a caller's score array: one workgroup per (g, b).
+__global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  __shared__ TopkShared sh;
+  const int nc = n_candidates(p.seq_lens[b], p.window, p.blk);
+  uint32_t* keys = smem;
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + p.max_blocks);
+  const int64_t t_stride = (int64_t)p.Hkv * p.max_blocks;
+  select_rows(p.scores + ((int64_t)b * p.T * p.Hkv + g) * p.max_blocks, t_stride, nc, p.T,
+              p.k_per_seq[b], p.k_max,
+              p.indices + ((int64_t)b * p.T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max,
+              p.n_sel + (int64_t)b * p.T * p.Hkv + g, p.Hkv,
+              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh);
+}
+
+// ------------------------------------------------------------ launchers
+
+size_t topk_lds_bytes(int max_cand) { return (size_t)max_cand * 4; }
+
+hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s) {
+  const dim3 grid(chunks, p.Hkv, p.B);
+  size_t lds = (size_t)p.T * p.D * 4;
+  if (p.fused_select) lds += topk_lds_bytes(p.score_cols) + (size_t)2 * p.k_max * 4;
+  if (p.D == 128) {
+    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<128, true>), grid, dim3(kThreads), lds, s, p);
+    else hipLaunchKernelGGL((score_kernel<128, false>), grid, dim3(kThreads), lds, s, p);
+  } else {
+    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<64, true>), grid, dim3(kThreads), lds, s, p);
+    else hipLaunchKernelGGL((score_kernel<64, false>), grid, dim3(kThreads), lds, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
+  const size_t lds = topk_lds_bytes(p.max_blocks) + (size_t)2 * p.k_max * 4;
+  hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,98 @@
+// skv_device.h -- device helpers shared by the gfx950 kernels of the
+// sparse-KV decode step (bf16 / fp8 e4m3fn decoding, MFMA wrappers,
+// cross-lane reductions).  Internal to the HIP library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+constexpr int kWave = 64;
+constexpr int kWaves = 4;               // waves per workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// ---------------------------------------------------------------- numbers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
+
+// Two OCP e4m3fn codes (bytes 0,1 of w when !HI, bytes 2,3 when HI) -> fp32.
+// gfx950's conversion instruction decodes the OCP encoding exactly.
+template <bool HI>
+__device__ __forceinline__ float2 fp8x2_to_f32(uint32_t w) {
+  auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  return make_float2(v[0], v[1]);
+}
+
+// Four e4m3fn codes -> four bf16 packed in two words.  Exact: an e4m3fn value
+// has a 4-bit significand and an exponent well inside bf16's range, so the
+// upper half of its fp32 image is the value itself.
+__device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
+  float2 a = fp8x2_to_f32<false>(w);
+  float2 b = fp8x2_to_f32<true>(w);
+  uint2 r;
+  r.x = (__float_as_uint(a.x) >> 16) | (__float_as_uint(a.y) & 0xffff0000u);
+  r.y = (__float_as_uint(b.x) >> 16) | (__float_as_uint(b.y) & 0xffff0000u);
+  return r;
+}
+
+// Sixteen e4m3fn codes -> sixteen bf16.
+__device__ __forceinline__ void fp8x16_to_bf16x16(uint4 c, uint4& lo, uint4& hi) {
+  uint2 a = fp8x4_to_bf16x4(c.x), b = fp8x4_to_bf16x4(c.y);
+  uint2 d = fp8x4_to_bf16x4(c.z), e = fp8x4_to_bf16x4(c.w);
+  lo = make_uint4(a.x, a.y, b.x, b.y);
+  hi = make_uint4(d.x, d.y, e.x, e.y);
+}
+
+// Order-preserving map of an fp32 score to an unsigned key (larger score ->
+// larger key).  -0 is folded onto +0 so that equal scores give equal keys;
+// NaN maps to the smallest key.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s != s) return 0u;
+  if (s == 0.0f) s = 0.0f;
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- lanes
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, kWave); }
+
+// Compiler and LDS ordering point between one wave's LDS writes and its own
+// later reads (LDS operations of a wave complete in order).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+}  // namespace skv

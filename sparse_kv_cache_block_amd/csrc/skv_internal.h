@@ -1,0 +1,114 @@
+// skv_internal.h -- parameter blocks and launchers shared between the C ABI
+// (sparsekv.hip) and the kernel translation units.  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sparsekv.h"
+
+namespace skv {
+
+// ------------------------------------------------------------ scoring / top-k
+struct ScoreParams {
+  const void* q;            // [B][T][Hq][d]
+  const void* landmarks;    // [B][Hkv][max_blocks][d]
+  const int32_t* seq_lens;
+  float* scores;            // [B][T][Hkv][score_cols]
+  int score_cols;           // max_blocks (standalone) or max candidates (fused)
+  int B, T, Hq, Hkv, G, D, blk, max_blocks, window;
+  int q_f32, lm_f32;        // 1 when q / landmarks are fp32, else bf16
+  int rows_per_chunk;
+  int fused_select;         // 1: last-arriving workgroup of (b, g) runs the top-k
+  // fused selection outputs
+  const int32_t* k_per_seq;
+  int32_t* indices;         // [B][T][Hkv][k_max]
+  int32_t* n_sel;           // [B][T][Hkv]
+  float* overlap;           // [B][Hkv] or null
+  int k_max;
+  unsigned* counters;       // [B][Hkv], zero between calls
+};
+
+struct TopkParams {
+  const float* scores;      // [B][T][Hkv][max_blocks]
+  const int32_t* seq_lens;
+  const int32_t* k_per_seq;
+  int32_t* indices;
+  int32_t* n_sel;
+  float* overlap;
+  int B, T, Hkv, blk, max_blocks, window, k_max;
+};
+
+// ------------------------------------------------------------------ attention
+struct AttnParams {
+  int kv;                   // KvKind of K/V
+  const void* q;            // [B][T][Hq][d]; token 0 attended
+  int B, T, Hq, Hkv, G, D, blk, window, max_blocks, k_max;
+  float qk_scale;           // log2(e) / sqrt(d)
+  // sparse part
+  int sparse_kind;          // SKV_SRC_PAGED or SKV_SRC_STAGED
+  const void* sk;
+  const void* sv;
+  const float* sks;
+  const float* svs;
+  const int32_t* block_table;
+  int64_t stride_block, stride_head;  // pool element strides
+  const int32_t* indices;   // [B][T][Hkv][k_max] (token 0 rows used)
+  const int32_t* n_sel;     // [B][T][Hkv]
+  // window part
+  int window_kind;          // SKV_SRC_PAGED or SKV_SRC_WINDOW
+  const void* wk;
+  const void* wv;
+  const float* wks;
+  const float* wvs;
+  const int32_t* window_table;  // block table for a PAGED window
+  const int32_t* seq_lens;
+  // split-K layout
+  int n_sparse_splits, n_window_splits, bps, bpw;
+  float* partials;          // [B][Hkv][splits][G][d + 2]
+  unsigned* counters;       // [B][Hkv]
+  float* out;               // [B][Hq][d]
+  float* lse;               // [B][Hq] or null
+};
+
+// --------------------------------------------------------------------- gather
+struct GatherParams {
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scales;
+  const float* v_scales;
+  const int32_t* block_table;
+  const int32_t* indices;
+  const int32_t* n_sel;
+  void* k_stage;
+  void* v_stage;
+  float* k_stage_scales;
+  float* v_stage_scales;
+  int B, T, Hkv, max_blocks, k_max;
+  int64_t stride_block, stride_head;  // elements
+  int64_t chunk_bytes;      // blk * d * element size
+  int elem_bytes;
+  int has_scales;
+};
+
+// Launch shapes decided on the host; the workspace layout depends on them.
+struct Plan {
+  int max_cand;             // upper bound of candidates per sequence
+  int rows_per_chunk, score_chunks;
+  int bps, bpw, n_sparse_splits, n_window_splits;
+  size_t off_score_counters, off_attn_counters, off_scores, off_partials, total_bytes;
+};
+
+Plan make_plan(const skv_problem& pr);
+
+hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s);
+hipError_t launch_topk(const TopkParams& p, hipStream_t s);
+hipError_t launch_attend(const AttnParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+
+// LDS bytes the score kernel needs for a fused selection over max_cand keys.
+size_t topk_lds_bytes(int max_cand);
+
+}  // namespace skv

@@ -1,0 +1,590 @@
+// sparsekv.hip -- the C ABI declared in include/sparsekv.h: argument
+// validation, launch planning, workspace carving, stream/event ordering.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "skv_device.h"
+#include "skv_internal.h"
+
+namespace skv {
+namespace {
+
+thread_local char g_err[512] = "";
+
+skv_status fail(skv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+skv_status fail(skv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+skv_status hip_fail(hipError_t e, const char* what) {
+  return fail(SKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SKV_TRY_HIP(expr, what)                 \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+#define SKV_TRY(expr)                  \
+  do {                                 \
+    skv_status s_ = (expr);            \
+    if (s_ != SKV_OK) return s_;       \
+  } while (0)
+
+int elem_bytes(int dt) { return dt == SKV_F32 ? 4 : dt == SKV_BF16 ? 2 : 1; }
+
+int kv_kind(int dt) { return dt == SKV_F32 ? KV_F32 : dt == SKV_BF16 ? KV_BF16 : KV_FP8; }
+
+skv_status check_problem(const skv_problem* pr) {
+  if (!pr) return fail(SKV_E_NULL, "problem is NULL");
+  const skv_problem& p = *pr;
+  if (p.batch < 1 || p.n_q_heads < 1 || p.n_kv_heads < 1 || p.head_dim < 1 || p.block_size < 1 ||
+      p.max_blocks_per_seq < 1 || p.n_pool_blocks < 1 || p.window < 0 || p.k_max < 1)
+    return fail(SKV_E_SHAPE, "non-positive size in problem");
+  if (p.n_q_tokens != 1 && p.n_q_tokens != 2)
+    return fail(SKV_E_SHAPE, "n_q_tokens must be 1 or 2 (got %d)", p.n_q_tokens);
+  if (p.n_q_heads % p.n_kv_heads != 0)
+    return fail(SKV_E_SHAPE, "n_q_heads %d is not a multiple of n_kv_heads %d", p.n_q_heads,
+                p.n_kv_heads);
+  if (p.k_max > p.max_blocks_per_seq)
+    return fail(SKV_E_SHAPE, "k_max %d exceeds max_blocks_per_seq %d", p.k_max, p.max_blocks_per_seq);
+  if (p.pool_stride_block < 0 || p.pool_stride_head < 0)
+    return fail(SKV_E_SHAPE, "negative pool stride");
+  for (int dt : {p.q_dtype, p.kv_dtype, p.landmark_dtype})
+    if (dt < SKV_F32 || dt > SKV_FP8_E4M3FN) return fail(SKV_E_DTYPE, "unknown dtype code %d", dt);
+  if (p.pool_location != SKV_POOL_DEVICE && p.pool_location != SKV_POOL_HOST)
+    return fail(SKV_E_SHAPE, "unknown pool_location %d", p.pool_location);
+  const int G = p.n_q_heads / p.n_kv_heads;
+  if (G > 8) return fail(SKV_E_UNSUPPORTED, "group size %d > 8", G);
+  if (p.head_dim != 64 && p.head_dim != 128)
+    return fail(SKV_E_UNSUPPORTED, "head_dim %d not in {64, 128}", p.head_dim);
+  if (p.block_size != 16 && p.block_size != 32 && p.block_size != 64)
+    return fail(SKV_E_UNSUPPORTED, "block_size %d not in {16, 32, 64}", p.block_size);
+  if (p.max_blocks_per_seq > 16384)
+    return fail(SKV_E_UNSUPPORTED, "max_blocks_per_seq %d > 16384", p.max_blocks_per_seq);
+  if (p.q_dtype == SKV_FP8_E4M3FN || p.landmark_dtype == SKV_FP8_E4M3FN)
+    return fail(SKV_E_UNSUPPORTED, "fp8 queries or landmarks");
+  if (p.kv_dtype == SKV_F32 && p.q_dtype != SKV_F32)
+    return fail(SKV_E_UNSUPPORTED, "fp32 K/V needs fp32 queries");
+  if (p.kv_dtype != SKV_F32 && p.q_dtype != SKV_BF16)
+    return fail(SKV_E_UNSUPPORTED, "bf16/fp8 K/V needs bf16 queries");
+  return SKV_OK;
+}
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+Plan make_plan(const skv_problem& p) {
+  Plan pl{};
+  const int G = p.n_q_heads / p.n_kv_heads;
+  const int blk = p.block_size, D = p.head_dim;
+  pl.max_cand = p.max_blocks_per_seq - p.window / blk;
+  if (pl.max_cand < 0) pl.max_cand = 0;
+  const int pairs = p.batch * p.n_kv_heads;
+  // scoring: rows per workgroup chunk, aiming at ~2048 workgroups
+  const int lm_es = p.landmark_dtype == SKV_F32 ? 4 : 2;
+  const int rps = 4 * (64 / (D * lm_es / 16));
+  int rows = (int)(((int64_t)pl.max_cand * pairs + 2047) / 2048);
+  rows = round_up(rows < 64 ? 64 : rows, rps);
+  if (rows > 1024) rows = 1024;
+  pl.rows_per_chunk = rows;
+  pl.score_chunks = pl.max_cand > 0 ? (pl.max_cand + rows - 1) / rows : 1;
+  // attention: blocks per split, aiming at ~2048 sparse workgroups
+  int bps = (int)(((int64_t)pairs * p.k_max + 2047) / 2048);
+  bps = round_up(bps < 4 ? 4 : bps, 4);
+  if (bps > 32) bps = 32;
+  pl.bps = bps;
+  pl.n_sparse_splits = (p.k_max + bps - 1) / bps;
+  const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
+  if (nwb == 0) {
+    pl.bpw = 1;
+    pl.n_window_splits = 0;
+  } else {
+    const int splits = (nwb + bps - 1) / bps;
+    pl.bpw = (nwb + splits - 1) / splits;
+    pl.n_window_splits = splits;
+  }
+  const int total = pl.n_sparse_splits + pl.n_window_splits;
+  size_t off = 0;
+  pl.off_score_counters = off;
+  off = align256(off + (size_t)pairs * 4);
+  pl.off_attn_counters = off;
+  off = align256(off + (size_t)pairs * 4);
+  pl.off_scores = off;
+  off = align256(off + (size_t)pairs * p.n_q_tokens * (pl.max_cand > 0 ? pl.max_cand : 1) * 4);
+  pl.off_partials = off;
+  off = align256(off + (size_t)pairs * total * G * (D + 2) * 4);
+  pl.total_bytes = off;
+  return pl;
+}
+
+namespace {
+
+ScoreParams score_params(const skv_problem& p, const void* q, const void* lm, const int32_t* seq_lens) {
+  ScoreParams s{};
+  s.q = q;
+  s.landmarks = lm;
+  s.seq_lens = seq_lens;
+  s.B = p.batch;
+  s.T = p.n_q_tokens;
+  s.Hq = p.n_q_heads;
+  s.Hkv = p.n_kv_heads;
+  s.G = p.n_q_heads / p.n_kv_heads;
+  s.D = p.head_dim;
+  s.blk = p.block_size;
+  s.max_blocks = p.max_blocks_per_seq;
+  s.window = p.window;
+  s.q_f32 = p.q_dtype == SKV_F32;
+  s.lm_f32 = p.landmark_dtype == SKV_F32;
+  s.k_max = p.k_max;
+  return s;
+}
+
+AttnParams attn_params(const skv_problem& p, const Plan& pl, const void* q, const int32_t* seq_lens,
+                       float* out, float* lse, char* ws) {
+  AttnParams a{};
+  a.kv = kv_kind(p.kv_dtype);
+  a.q = q;
+  a.B = p.batch;
+  a.T = p.n_q_tokens;
+  a.Hq = p.n_q_heads;
+  a.Hkv = p.n_kv_heads;
+  a.G = p.n_q_heads / p.n_kv_heads;
+  a.D = p.head_dim;
+  a.blk = p.block_size;
+  a.window = p.window;
+  a.max_blocks = p.max_blocks_per_seq;
+  a.k_max = p.k_max;
+  a.qk_scale = kLog2e / std::sqrt((float)p.head_dim);
+  a.stride_block = p.pool_stride_block;
+  a.stride_head = p.pool_stride_head;
+  a.seq_lens = seq_lens;
+  a.n_sparse_splits = pl.n_sparse_splits;
+  a.n_window_splits = pl.n_window_splits;
+  a.bps = pl.bps;
+  a.bpw = pl.bpw;
+  a.partials = reinterpret_cast<float*>(ws + pl.off_partials);
+  a.counters = reinterpret_cast<unsigned*>(ws + pl.off_attn_counters);
+  a.out = out;
+  a.lse = lse;
+  return a;
+}
+
+skv_status set_source(const skv_problem& p, AttnParams& a, const skv_kv_source* src, bool sparse) {
+  if (!src) return fail(SKV_E_NULL, "%s source is NULL", sparse ? "sparse" : "window");
+  if (!src->k || !src->v) return fail(SKV_E_NULL, "%s source K/V is NULL", sparse ? "sparse" : "window");
+  const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
+  if (fp8 && (!src->k_scales || !src->v_scales))
+    return fail(SKV_E_NULL, "fp8 %s source needs scales", sparse ? "sparse" : "window");
+  if (sparse) {
+    if (src->kind != SKV_SRC_PAGED && src->kind != SKV_SRC_STAGED)
+      return fail(SKV_E_UNSUPPORTED, "sparse source kind %d", src->kind);
+    if (src->kind == SKV_SRC_PAGED && !src->block_table)
+      return fail(SKV_E_NULL, "paged sparse source needs a block table");
+    a.sparse_kind = src->kind;
+    a.sk = src->k;
+    a.sv = src->v;
+    a.sks = fp8 ? src->k_scales : nullptr;
+    a.svs = fp8 ? src->v_scales : nullptr;
+    a.block_table = src->block_table;
+  } else {
+    if (src->kind != SKV_SRC_PAGED && src->kind != SKV_SRC_WINDOW)
+      return fail(SKV_E_UNSUPPORTED, "window source kind %d", src->kind);
+    if (src->kind == SKV_SRC_PAGED && !src->block_table)
+      return fail(SKV_E_NULL, "paged window source needs a block table");
+    if (src->kind == SKV_SRC_WINDOW) {
+      if (fp8) return fail(SKV_E_UNSUPPORTED, "fp8 window buffers");
+      if (p.window % p.block_size != 0)
+        return fail(SKV_E_SHAPE, "window buffer needs window %% block_size == 0");
+    }
+    a.window_kind = src->kind;
+    a.wk = src->k;
+    a.wv = src->v;
+    a.wks = fp8 ? src->k_scales : nullptr;
+    a.wvs = fp8 ? src->v_scales : nullptr;
+    a.window_table = src->block_table;
+  }
+  return SKV_OK;
+}
+
+skv_status check_ws(const Plan& pl, void* ws, size_t bytes) {
+  if (!ws) return fail(SKV_E_WORKSPACE, "workspace is NULL");
+  if (bytes < pl.total_bytes)
+    return fail(SKV_E_WORKSPACE, "workspace %zu bytes < %zu needed", bytes, pl.total_bytes);
+  return SKV_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Scoring with the in-kernel selection (first half of a decode step).
+skv_status enqueue_score_select(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                                const skv_step_outputs& out, char* ws, hipStream_t s) {
+  ScoreParams sp = score_params(p, in.q, in.landmarks, in.seq_lens);
+  sp.scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  sp.score_cols = pl.max_cand > 0 ? pl.max_cand : 1;
+  sp.rows_per_chunk = pl.rows_per_chunk;
+  sp.fused_select = 1;
+  sp.k_per_seq = in.k_per_seq;
+  sp.indices = out.indices;
+  sp.n_sel = out.n_sel;
+  sp.overlap = p.n_q_tokens == 2 ? out.overlap : nullptr;
+  sp.counters = reinterpret_cast<unsigned*>(ws + pl.off_score_counters);
+  SKV_TRY_HIP(launch_score(sp, pl.score_chunks, s), "score/top-k launch");
+  return SKV_OK;
+}
+
+skv_status check_step_io(const skv_problem& p, const skv_step_inputs* in, const skv_step_outputs* out) {
+  if (!in || !out) return fail(SKV_E_NULL, "inputs/outputs NULL");
+  if (!in->q || !in->landmarks || !in->block_table || !in->seq_lens || !in->k_per_seq)
+    return fail(SKV_E_NULL, "a required input pointer is NULL");
+  if (!out->indices || !out->n_sel || !out->out)
+    return fail(SKV_E_NULL, "a required output pointer is NULL");
+  if (p.pool_location == SKV_POOL_DEVICE && (!in->k_pool || !in->v_pool))
+    return fail(SKV_E_NULL, "K/V pool is NULL");
+  if (p.pool_location == SKV_POOL_HOST && (!in->k_pool || !in->v_pool))
+    return fail(SKV_E_NULL, "host K/V pool is NULL");
+  if (p.pool_location == SKV_POOL_HOST && p.window > 0 && (!in->window_k || !in->window_v))
+    return fail(SKV_E_NULL, "host pools need HBM window buffers");
+  if (p.kv_dtype == SKV_FP8_E4M3FN && (!in->k_scales || !in->v_scales))
+    return fail(SKV_E_NULL, "fp8 pools need scales");
+  return SKV_OK;
+}
+
+skv_status enqueue_attend_paged(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                                const skv_step_outputs& out, char* ws, hipStream_t s) {
+  AttnParams a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
+  skv_kv_source sparse{SKV_SRC_PAGED, in.k_pool, in.v_pool, in.k_scales, in.v_scales, in.block_table};
+  skv_kv_source win = in.window_k
+      ? skv_kv_source{SKV_SRC_WINDOW, in.window_k, in.window_v, nullptr, nullptr, nullptr}
+      : sparse;
+  SKV_TRY(set_source(p, a, &sparse, true));
+  SKV_TRY(set_source(p, a, &win, false));
+  a.indices = out.indices;
+  a.n_sel = out.n_sel;
+  SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  return SKV_OK;
+}
+
+skv_status enqueue_host_layer(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                              const skv_step_outputs& out, void* k_stage, void* v_stage,
+                              float* k_stage_scales, float* v_stage_scales, char* ws,
+                              hipStream_t s, hipStream_t cs, hipEvent_t ev_sel, hipEvent_t ev_gather,
+                              hipEvent_t slot_free) {
+  // the copy stream waits for this layer's indices (and for the slot to be free)
+  SKV_TRY_HIP(hipEventRecord(ev_sel, s), "event record");
+  SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel, 0), "stream wait");
+  if (slot_free) SKV_TRY_HIP(hipStreamWaitEvent(cs, slot_free, 0), "stream wait");
+  GatherParams gp{};
+  gp.k_pool = in.k_pool;
+  gp.v_pool = in.v_pool;
+  gp.k_scales = in.k_scales;
+  gp.v_scales = in.v_scales;
+  gp.block_table = in.block_table;
+  gp.indices = out.indices;
+  gp.n_sel = out.n_sel;
+  gp.k_stage = k_stage;
+  gp.v_stage = v_stage;
+  gp.k_stage_scales = k_stage_scales;
+  gp.v_stage_scales = v_stage_scales;
+  gp.B = p.batch;
+  gp.T = p.n_q_tokens;
+  gp.Hkv = p.n_kv_heads;
+  gp.max_blocks = p.max_blocks_per_seq;
+  gp.k_max = p.k_max;
+  gp.stride_block = p.pool_stride_block;
+  gp.stride_head = p.pool_stride_head;
+  gp.elem_bytes = elem_bytes(p.kv_dtype);
+  gp.chunk_bytes = (int64_t)p.block_size * p.head_dim * gp.elem_bytes;
+  gp.has_scales = p.kv_dtype == SKV_FP8_E4M3FN;
+  SKV_TRY_HIP(launch_gather(gp, cs), "gather launch");
+  SKV_TRY_HIP(hipEventRecord(ev_gather, cs), "event record");
+  SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather, 0), "stream wait");
+  AttnParams a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
+  skv_kv_source sparse{SKV_SRC_STAGED, k_stage, v_stage, k_stage_scales, v_stage_scales, nullptr};
+  SKV_TRY(set_source(p, a, &sparse, true));
+  if (p.window > 0) {
+    skv_kv_source win{SKV_SRC_WINDOW, in.window_k, in.window_v, nullptr, nullptr, nullptr};
+    SKV_TRY(set_source(p, a, &win, false));
+  } else {
+    a.window_kind = SKV_SRC_WINDOW;  // no window splits are launched
+  }
+  a.indices = out.indices;
+  a.n_sel = out.n_sel;
+  SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  return SKV_OK;
+}
+
+struct EventSet {
+  hipEvent_t e[64] = {};
+  int n = 0;
+  ~EventSet() {
+    for (int i = 0; i < n; ++i) (void)hipEventDestroy(e[i]);
+  }
+  hipError_t make(int count) {
+    for (; n < count; ++n) {
+      hipError_t r = hipEventCreateWithFlags(&e[n], hipEventDisableTiming);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+};
+
+}  // namespace
+}  // namespace skv
+
+using namespace skv;
+
+extern "C" {
+
+const char* sparsekv_status_string(int status) {
+  switch (status) {
+    case SKV_OK: return "ok";
+    case SKV_E_NULL: return "null pointer";
+    case SKV_E_SHAPE: return "bad shape";
+    case SKV_E_DTYPE: return "bad dtype";
+    case SKV_E_UNSUPPORTED: return "unsupported combination";
+    case SKV_E_WORKSPACE: return "workspace missing or too small";
+    case SKV_E_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* sparsekv_last_error(void) { return g_err; }
+
+const char* sparsekv_version(void) { return "0.1.0"; }
+
+skv_status sparsekv_workspace_size(const skv_problem* pr, size_t* bytes) {
+  SKV_TRY(check_problem(pr));
+  if (!bytes) return fail(SKV_E_NULL, "bytes is NULL");
+  *bytes = make_plan(*pr).total_bytes;
+  return SKV_OK;
+}
+
+skv_status sparsekv_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return fail(SKV_E_NULL, "workspace is NULL");
+  SKV_TRY_HIP(launch_fill_zero(workspace, bytes, as_stream(stream)), "workspace fill");
+  return SKV_OK;
+}
+
+skv_status sparsekv_score(const skv_problem* pr, const void* q, const void* landmarks,
+                          const int32_t* seq_lens, float* scores, void* stream) {
+  SKV_TRY(check_problem(pr));
+  if (!q || !landmarks || !seq_lens || !scores) return fail(SKV_E_NULL, "score: NULL argument");
+  const skv_problem& p = *pr;
+  ScoreParams sp = score_params(p, q, landmarks, seq_lens);
+  sp.scores = scores;
+  sp.score_cols = p.max_blocks_per_seq;
+  const int lm_es = p.landmark_dtype == SKV_F32 ? 4 : 2;
+  const int rps = 4 * (64 / (p.head_dim * lm_es / 16));
+  sp.rows_per_chunk = rps * 16;
+  sp.fused_select = 0;
+  const int chunks = (p.max_blocks_per_seq + sp.rows_per_chunk - 1) / sp.rows_per_chunk;
+  SKV_TRY_HIP(launch_score(sp, chunks, as_stream(stream)), "score launch");
+  return SKV_OK;
+}
+
+skv_status sparsekv_topk(const skv_problem* pr, const float* scores, const int32_t* seq_lens,
+                         const int32_t* k_per_seq, int32_t* indices, int32_t* n_sel, float* overlap,
+                         void* stream) {
+  SKV_TRY(check_problem(pr));
+  if (!scores || !seq_lens || !k_per_seq || !indices || !n_sel)
+    return fail(SKV_E_NULL, "topk: NULL argument");
+  const skv_problem& p = *pr;
+  TopkParams tp{};
+  tp.scores = scores;
+  tp.seq_lens = seq_lens;
+  tp.k_per_seq = k_per_seq;
+  tp.indices = indices;
+  tp.n_sel = n_sel;
+  tp.overlap = p.n_q_tokens == 2 ? overlap : nullptr;
+  tp.B = p.batch;
+  tp.T = p.n_q_tokens;
+  tp.Hkv = p.n_kv_heads;
+  tp.blk = p.block_size;
+  tp.max_blocks = p.max_blocks_per_seq;
+  tp.window = p.window;
+  tp.k_max = p.k_max;
+  SKV_TRY_HIP(launch_topk(tp, as_stream(stream)), "top-k launch");
+  return SKV_OK;
+}
+
+skv_status sparsekv_gather(const skv_problem* pr, const void* k_pool, const void* v_pool,
+                           const float* k_scales, const float* v_scales, const int32_t* block_table,
+                           const int32_t* indices, const int32_t* n_sel, void* k_stage, void* v_stage,
+                           float* k_stage_scales, float* v_stage_scales, void* stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  if (!k_pool || !v_pool || !block_table || !indices || !n_sel || !k_stage || !v_stage)
+    return fail(SKV_E_NULL, "gather: NULL argument");
+  const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
+  if (fp8 && (!k_scales || !v_scales || !k_stage_scales || !v_stage_scales))
+    return fail(SKV_E_NULL, "gather: fp8 needs pool and stage scales");
+  GatherParams gp{};
+  gp.k_pool = k_pool;
+  gp.v_pool = v_pool;
+  gp.k_scales = k_scales;
+  gp.v_scales = v_scales;
+  gp.block_table = block_table;
+  gp.indices = indices;
+  gp.n_sel = n_sel;
+  gp.k_stage = k_stage;
+  gp.v_stage = v_stage;
+  gp.k_stage_scales = k_stage_scales;
+  gp.v_stage_scales = v_stage_scales;
+  gp.B = p.batch;
+  gp.T = p.n_q_tokens;
+  gp.Hkv = p.n_kv_heads;
+  gp.max_blocks = p.max_blocks_per_seq;
+  gp.k_max = p.k_max;
+  gp.stride_block = p.pool_stride_block;
+  gp.stride_head = p.pool_stride_head;
+  gp.elem_bytes = elem_bytes(p.kv_dtype);
+  gp.chunk_bytes = (int64_t)p.block_size * p.head_dim * gp.elem_bytes;
+  gp.has_scales = fp8;
+  SKV_TRY_HIP(launch_gather(gp, as_stream(stream)), "gather launch");
+  return SKV_OK;
+}
+
+skv_status sparsekv_attend(const skv_problem* pr, const void* q, const skv_kv_source* sparse,
+                           const int32_t* indices, const int32_t* n_sel, const skv_kv_source* window,
+                           const int32_t* seq_lens, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  if (!q || !indices || !n_sel || !seq_lens || !out) return fail(SKV_E_NULL, "attend: NULL argument");
+  const Plan pl = make_plan(p);
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  char* ws = static_cast<char*>(workspace);
+  AttnParams a = attn_params(p, pl, q, seq_lens, out, lse, ws);
+  SKV_TRY(set_source(p, a, sparse, true));
+  if (p.window > 0) SKV_TRY(set_source(p, a, window, false));
+  else a.window_kind = SKV_SRC_WINDOW;
+  a.indices = indices;
+  a.n_sel = n_sel;
+  SKV_TRY_HIP(launch_attend(a, as_stream(stream)), "attention launch");
+  return SKV_OK;
+}
+
+skv_status sparsekv_decode_step(const skv_problem* pr, const skv_step_inputs* in,
+                                const skv_step_outputs* out, void* k_stage, void* v_stage,
+                                float* k_stage_scales, float* v_stage_scales, void* workspace,
+                                size_t workspace_bytes, void* stream, void* copy_stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  SKV_TRY(check_step_io(p, in, out));
+  const Plan pl = make_plan(p);
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = as_stream(stream);
+  if (p.pool_location == SKV_POOL_DEVICE) {
+    SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
+    return enqueue_attend_paged(p, pl, *in, *out, ws, s);
+  }
+  if (!k_stage || !v_stage) return fail(SKV_E_NULL, "host pools need staging buffers");
+  if (p.kv_dtype == SKV_FP8_E4M3FN && (!k_stage_scales || !v_stage_scales))
+    return fail(SKV_E_NULL, "fp8 staging needs scale buffers");
+  hipStream_t cs = copy_stream ? as_stream(copy_stream) : s;
+  EventSet ev;
+  SKV_TRY_HIP(ev.make(2), "event create");
+  SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
+  return enqueue_host_layer(p, pl, *in, *out, k_stage, v_stage, k_stage_scales, v_stage_scales, ws,
+                            s, cs, ev.e[0], ev.e[1], nullptr);
+}
+
+skv_status sparsekv_decode_layers(const skv_problem* pr, int32_t n_layers, const skv_step_inputs* in,
+                                  const skv_step_outputs* out, void* const* k_stage,
+                                  void* const* v_stage, float* const* k_stage_scales,
+                                  float* const* v_stage_scales, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* copy_stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  if (p.pool_location != SKV_POOL_HOST)
+    return fail(SKV_E_UNSUPPORTED, "decode_layers pipelines host pools only");
+  if (n_layers < 1 || n_layers > 16) return fail(SKV_E_SHAPE, "n_layers %d not in [1, 16]", n_layers);
+  if (!in || !out || !k_stage || !v_stage) return fail(SKV_E_NULL, "decode_layers: NULL argument");
+  for (int l = 0; l < n_layers; ++l) SKV_TRY(check_step_io(p, &in[l], &out[l]));
+  for (int slot = 0; slot < 2 && slot < n_layers; ++slot) {
+    if (!k_stage[slot] || !v_stage[slot]) return fail(SKV_E_NULL, "staging slot %d is NULL", slot);
+    if (p.kv_dtype == SKV_FP8_E4M3FN &&
+        (!k_stage_scales || !v_stage_scales || !k_stage_scales[slot] || !v_stage_scales[slot]))
+      return fail(SKV_E_NULL, "fp8 staging slot %d needs scales", slot);
+  }
+  const Plan pl = make_plan(p);
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = as_stream(stream);
+  hipStream_t cs = copy_stream ? as_stream(copy_stream) : s;
+  EventSet ev;
+  SKV_TRY_HIP(ev.make(3 * n_layers), "event create");
+  hipEvent_t* ev_sel = ev.e;
+  hipEvent_t* ev_gather = ev.e + n_layers;
+  hipEvent_t* ev_attn = ev.e + 2 * n_layers;
+  // Selection of every layer first (the per-layer queries are given up front,
+  // standing in for the predicted indices of a lookahead scheme), so the copy
+  // stream can run ahead; slot l % 2 is reused once layer l-2's attention is done.
+  for (int l = 0; l < n_layers; ++l) {
+    SKV_TRY(enqueue_score_select(p, pl, in[l], out[l], ws, s));
+    SKV_TRY_HIP(hipEventRecord(ev_sel[l], s), "event record");
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    const int slot = l & 1;
+    SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel[l], 0), "stream wait");
+    if (l >= 2) SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_attn[l - 2], 0), "stream wait");
+    GatherParams gp{};
+    gp.k_pool = in[l].k_pool;
+    gp.v_pool = in[l].v_pool;
+    gp.k_scales = in[l].k_scales;
+    gp.v_scales = in[l].v_scales;
+    gp.block_table = in[l].block_table;
+    gp.indices = out[l].indices;
+    gp.n_sel = out[l].n_sel;
+    gp.k_stage = k_stage[slot];
+    gp.v_stage = v_stage[slot];
+    gp.k_stage_scales = k_stage_scales ? k_stage_scales[slot] : nullptr;
+    gp.v_stage_scales = v_stage_scales ? v_stage_scales[slot] : nullptr;
+    gp.B = p.batch;
+    gp.T = p.n_q_tokens;
+    gp.Hkv = p.n_kv_heads;
+    gp.max_blocks = p.max_blocks_per_seq;
+    gp.k_max = p.k_max;
+    gp.stride_block = p.pool_stride_block;
+    gp.stride_head = p.pool_stride_head;
+    gp.elem_bytes = elem_bytes(p.kv_dtype);
+    gp.chunk_bytes = (int64_t)p.block_size * p.head_dim * gp.elem_bytes;
+    gp.has_scales = p.kv_dtype == SKV_FP8_E4M3FN;
+    SKV_TRY_HIP(launch_gather(gp, cs), "gather launch");
+    SKV_TRY_HIP(hipEventRecord(ev_gather[l], cs), "event record");
+    SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather[l], 0), "stream wait");
+    AttnParams a = attn_params(p, pl, in[l].q, in[l].seq_lens, out[l].out, out[l].lse, ws);
+    skv_kv_source sparse{SKV_SRC_STAGED, k_stage[slot], v_stage[slot],
+                         k_stage_scales ? k_stage_scales[slot] : nullptr,
+                         v_stage_scales ? v_stage_scales[slot] : nullptr, nullptr};
+    SKV_TRY(set_source(p, a, &sparse, true));
+    if (p.window > 0) {
+      skv_kv_source win{SKV_SRC_WINDOW, in[l].window_k, in[l].window_v, nullptr, nullptr, nullptr};
+      SKV_TRY(set_source(p, a, &win, false));
+    } else {
+      a.window_kind = SKV_SRC_WINDOW;
+    }
+    a.indices = out[l].indices;
+    a.n_sel = out[l].n_sel;
+    SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+    SKV_TRY_HIP(hipEventRecord(ev_attn[l], s), "event record");
+  }
+  // the caller's stream ends after every layer's attention; join the copy stream too
+  if (cs != s) SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather[n_layers - 1], 0), "stream wait");
+  return SKV_OK;
+}
+
+}  // extern "C"

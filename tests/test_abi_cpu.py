@@ -1,0 +1,114 @@
+"""The C-ABI library loads and exports every entry point its header declares,
+and its host-side validation rejects bad arguments before any launch.
+No GPU work is issued here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from sparse_kv_cache_block_amd import binding as B
+from sparse_kv_cache_block_amd import build as skv_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsekv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        skv_build.build()
+    return B.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsekv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ("sparsekv_score", "sparsekv_topk", "sparsekv_gather", "sparsekv_attend",
+                 "sparsekv_decode_step"):
+        assert name in syms
+    assert set(syms) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def _good_problem(**kw):
+    base = dict(B=2, T=1, Hq=8, Hkv=2, d=128, blk=32, max_blocks=64, n_pool_blocks=128,
+                stride_block=2 * 32 * 128, stride_head=32 * 128, window=64, k_max=8,
+                q_dtype="bf16", kv_dtype="bf16", landmark_dtype="bf16")
+    base.update(kw)
+    return B.make_problem(base["B"], base["T"], base["Hq"], base["Hkv"], base["d"], base["blk"],
+                          base["max_blocks"], base["n_pool_blocks"], base["stride_block"],
+                          base["stride_head"], base["window"], base["k_max"], base["q_dtype"],
+                          base["kv_dtype"], base["landmark_dtype"])
+
+
+def test_workspace_size_is_host_only(lib):
+    n = B.sparsekv_workspace_size(_good_problem())
+    assert n > 0 and n % 256 == 0
+    assert B.sparsekv_version().count(".") == 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), B.SKV_E_SHAPE),
+    (dict(T=3), B.SKV_E_SHAPE),
+    (dict(k_max=0), B.SKV_E_SHAPE),
+    (dict(k_max=65), B.SKV_E_SHAPE),
+    (dict(window=-1), B.SKV_E_SHAPE),
+    (dict(d=96), B.SKV_E_UNSUPPORTED),
+    (dict(blk=8), B.SKV_E_UNSUPPORTED),
+    (dict(Hq=32, Hkv=2), B.SKV_E_UNSUPPORTED),
+    (dict(kv_dtype="fp32"), B.SKV_E_UNSUPPORTED),
+    (dict(q_dtype=7), B.SKV_E_DTYPE),
+    (dict(max_blocks=20000, k_max=8), B.SKV_E_UNSUPPORTED),
+])
+def test_validation_rejects_before_launch(lib, kw, status):
+    pr = _good_problem(**kw)
+    n = C.c_size_t(0)
+    assert lib.sparsekv_workspace_size(C.byref(pr), C.byref(n)) == status
+    # a compute entry point with dummy (never dereferenced) pointers fails the same way
+    dummy = 0x1000
+    assert lib.sparsekv_score(C.byref(pr), dummy, dummy, dummy, dummy, None) == status
+    assert len(B.sparsekv_last_error()) > 0
+
+
+def test_null_pointers_rejected(lib):
+    pr = _good_problem()
+    assert lib.sparsekv_score(C.byref(pr), None, 0x1000, 0x1000, 0x1000, None) == B.SKV_E_NULL
+    assert lib.sparsekv_topk(C.byref(pr), 0x1000, 0x1000, 0x1000, None, 0x1000, None, None) == B.SKV_E_NULL
+    assert lib.sparsekv_score(None, 0x1000, 0x1000, 0x1000, 0x1000, None) == B.SKV_E_NULL
+
+
+def test_workspace_too_small_rejected(lib):
+    pr = _good_problem()
+    src = B.KvSource(B.SKV_SRC_PAGED, 0x1000, 0x1000, None, None, 0x1000)
+    st = lib.sparsekv_attend(C.byref(pr), 0x1000, C.byref(src), 0x1000, 0x1000, C.byref(src), 0x1000,
+                             0x1000, None, 0x1000, 16, None)
+    assert st == B.SKV_E_WORKSPACE
+
+
+def test_window_buffer_needs_aligned_window(lib):
+    pr = _good_problem(window=48)
+    n = B.sparsekv_workspace_size(pr)
+    src = B.KvSource(B.SKV_SRC_PAGED, 0x1000, 0x1000, None, None, 0x1000)
+    win = B.KvSource(B.SKV_SRC_WINDOW, 0x1000, 0x1000, None, None, None)
+    st = lib.sparsekv_attend(C.byref(pr), 0x1000, C.byref(src), 0x1000, 0x1000, C.byref(win), 0x1000,
+                             0x1000, None, 0x1000, n, None)
+    assert st == B.SKV_E_SHAPE
+
+
+def test_fp8_needs_scales(lib):
+    pr = _good_problem(kv_dtype="fp8")
+    n = B.sparsekv_workspace_size(pr)
+    src = B.KvSource(B.SKV_SRC_PAGED, 0x1000, 0x1000, None, None, 0x1000)
+    st = lib.sparsekv_attend(C.byref(pr), 0x1000, C.byref(src), 0x1000, 0x1000, C.byref(src), 0x1000,
+                             0x1000, None, 0x1000, n, None)
+    assert st == B.SKV_E_NULL

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Gates (selected indices bit-exact outside the 1e-5 relative exemption band of
+the k-th score; gathered bytes exact; attention output max-abs 2e-3 for bf16
+K/V, 8e-3 for fp8, and 1e-4 for the fp32 reference shape) on seeded inputs.
+Attention is compared against the oracle evaluated on the GPU's own index set,
+so an exempt near-tie swap is never counted as an attention error.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from sparse_kv_cache_block_amd import binding as B
+from sparse_kv_cache_block_amd import configs
+from sparse_kv_cache_block_amd.inputs import make_inputs
+from sparse_kv_cache_block_amd.step import DecodeStep, to_device_for
+from tests.common import HostArrays, check_indices, oracle_problem
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-3, "fp8": 8e-3}
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def compare_attention(inp, h, gpu_idx, gpu_nsel, gpu_out, gpu_lse, tol):
+    pr = oracle_problem(inp, k_max=gpu_idx.shape[-1])
+    o_out, o_lse = O.attend(pr, h.q, *h.pools(), h.block_table, h.seq_lens, gpu_idx, gpu_nsel)
+    err = float(np.max(np.abs(gpu_out.astype(np.float64) - o_out))) if o_out.size else 0.0
+    assert err <= tol, f"attention max-abs error {err} > {tol}"
+    fin = np.isfinite(o_lse)
+    assert np.array_equal(fin, np.isfinite(gpu_lse)), "lse finiteness differs"
+    if fin.any():
+        lerr = float(np.max(np.abs(gpu_lse[fin] - o_lse[fin])))
+        assert lerr <= tol, f"lse error {lerr} > {tol}"
+    assert np.all(gpu_lse[~fin] == -np.inf)
+    return err
+
+
+def run_step(wl, seq_lens=None, gen_device="cpu", mutate=None, k_max=None):
+    inp = make_inputs(wl, device=gen_device, seq_lens=seq_lens)
+    if mutate:
+        mutate(inp)
+    inp = inp.to("cpu") if gen_device != "cpu" else inp
+    dev = to_device_for(inp)
+    st = DecodeStep(dev, k_max=k_max)
+    st.run()
+    torch.cuda.synchronize()
+    return inp, st
+
+
+def check_step(wl, seq_lens=None, gen_device="cpu", mutate=None):
+    announce(f"decode_step {wl.name} B={wl.batch} L={wl.context} kv={wl.kv_dtype} T={wl.n_q_tokens} "
+             f"pool={wl.pool} seq_lens={seq_lens}")
+    inp, st = run_step(wl, seq_lens, gen_device, mutate)
+    h = HostArrays(inp)
+    pr = oracle_problem(inp)
+    orc = O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
+    gi, gn = _np(st.indices), _np(st.n_sel)
+    swaps = check_indices(gi, gn, orc["indices"], orc["n_sel"], orc["scores"], h.seq_lens,
+                          wl.window, wl.block_size)
+    err = compare_attention(inp, h, gi, gn, _np(st.out), _np(st.lse), TOL[wl.kv_dtype])
+    if wl.n_q_tokens == 2:
+        ov = O.overlap(pr, gi, gn)
+        np.testing.assert_allclose(_np(st.overlap), ov, rtol=0, atol=1e-6)
+    if swaps == 0:
+        # same selection: the end-to-end result matches the oracle's own decode step
+        assert float(np.max(np.abs(_np(st.out) - orc["out"]))) <= TOL[wl.kv_dtype]
+    print(f"[case] ok: max-abs err {err:.3g}, exempt swaps {swaps}", flush=True)
+    return inp, st
+
+
+# ------------------------------------------------------------ small shapes
+def test_tiny_reference_config():
+    check_step(configs.TINY)
+
+
+def test_llama32k_shape_small_context():
+    check_step(configs.LLAMA32K.scaled(batch=2, context=4096))
+
+
+def test_llama32k_shape_mixed_lengths():
+    check_step(configs.LLAMA32K.scaled(batch=4, context=4096), seq_lens=[4096, 1000, 513, 37])
+
+
+def test_ragged_small_poisoned():
+    check_step(configs.RAGGED.scaled(batch=6, context=8192, ragged_min=100))
+
+
+def test_dual_fp8_small():
+    check_step(configs.DUAL.scaled(batch=2, context=16384, window=1024))
+
+
+def test_host_pool_small():
+    check_step(configs.HOST.scaled(batch=2, context=8192))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(window=0),
+    dict(top_k=90),
+    dict(head_dim=64),
+    dict(block_size=16),
+    dict(block_size=64),
+    dict(n_q_heads=16, n_kv_heads=8),
+    dict(n_q_heads=8, n_kv_heads=1),
+])
+def test_bf16_variants(kw):
+    args = dict(batch=2, context=3000, top_k=24)
+    args.update(kw)
+    check_step(configs.LLAMA32K.scaled(**args), seq_lens=[3000, 2100])
+
+
+@pytest.mark.parametrize("kw", [dict(block_size=16), dict(block_size=32), dict(head_dim=64)])
+def test_fp8_variants(kw):
+    check_step(configs.DUAL.scaled(batch=2, context=4096, window=256, top_k=20, **kw))
+
+
+def test_fp32_variants():
+    check_step(configs.TINY.scaled(batch=2, head_dim=128, block_size=32), seq_lens=[4096, 777])
+
+
+def test_zero_query_ties_go_to_lowest_ids():
+    def zero_q(inp):
+        inp.q.zero_()
+    inp, st = check_step(configs.LLAMA32K.scaled(batch=2, context=4096), mutate=zero_q)
+    gi = _np(st.indices)
+    assert np.all(gi[:, 0, :, :] == np.arange(64)[None, None, :])
+
+
+def test_duplicated_landmarks_exact_ties():
+    def dup(inp):
+        inp.landmarks[:, :, 1::2] = inp.landmarks[:, :, 0::2]
+    check_step(configs.LLAMA32K.scaled(batch=2, context=4096, top_k=13), mutate=dup)
+
+
+def test_empty_and_window_only_sequences():
+    check_step(configs.LLAMA32K.scaled(batch=4, context=2048), seq_lens=[0, 1, 512, 513])
+
+
+def test_dual_identical_tokens_overlap_one():
+    def same(inp):
+        inp.q[:, 1] = inp.q[:, 0]
+    inp, st = check_step(configs.DUAL.scaled(batch=2, context=8192), mutate=same)
+    assert np.all(_np(st.overlap) == 1.0)
+
+
+# ------------------------------------------------------------ separate entry points
+def test_score_and_topk_entry_points():
+    wl = configs.DUAL.scaled(batch=2, context=8192, top_k=40)
+    announce("sparsekv_score + sparsekv_topk on the dual shape")
+    inp = make_inputs(wl, seq_lens=[8192, 5000])
+    dev = to_device_for(inp)
+    from sparse_kv_cache_block_amd.step import problem_for
+    pr = problem_for(dev)
+    scores = torch.empty((2, 2, wl.n_kv_heads, wl.max_blocks), dtype=torch.float32, device="cuda")
+    B.sparsekv_score(pr, dev.q, dev.landmarks, dev.seq_lens, scores)
+    idx = torch.empty((2, 2, wl.n_kv_heads, pr.k_max), dtype=torch.int32, device="cuda")
+    nsel = torch.empty((2, 2, wl.n_kv_heads), dtype=torch.int32, device="cuda")
+    ov = torch.empty((2, wl.n_kv_heads), dtype=torch.float32, device="cuda")
+    B.sparsekv_topk(pr, scores, dev.seq_lens, dev.k_per_seq, idx, nsel, ov)
+    torch.cuda.synchronize()
+    h = HostArrays(inp)
+    opr = oracle_problem(inp)
+    osc = O.scores(opr, h.q, h.landmarks, h.seq_lens)
+    gsc = _np(scores).astype(np.float64)
+    fin = np.isfinite(osc)
+    assert np.array_equal(fin, np.isfinite(gsc))
+    rel = np.abs(gsc[fin] - osc[fin]) / np.maximum(np.abs(osc[fin]), 1.0)
+    assert rel.max() < 1e-5, rel.max()
+    # top-k of the GPU's own fp32 scores must equal the oracle's selection on them, bit for bit
+    oi, on = O.select(opr, gsc, h.seq_lens, h.k_per_seq)
+    assert np.array_equal(_np(idx), oi) and np.array_equal(_np(nsel), on)
+    np.testing.assert_allclose(_np(ov), O.overlap(opr, oi, on), atol=1e-6)
+
+
+def test_gather_and_attend_entry_points():
+    for wl in (configs.LLAMA32K.scaled(batch=2, context=4096),
+               configs.DUAL.scaled(batch=2, context=8192, top_k=30)):
+        announce(f"sparsekv_gather + sparsekv_attend ({wl.name})")
+        inp, st = run_step(wl)
+        dev = st.inp
+        pr = st.pr
+        Bn, Hkv, km = wl.batch, wl.n_kv_heads, pr.k_max
+        shape = (Bn, Hkv, km, wl.block_size, wl.head_dim)
+        ks = torch.zeros(shape, dtype=dev.k_pool.dtype, device="cuda")
+        vs = torch.zeros(shape, dtype=dev.v_pool.dtype, device="cuda")
+        kss = vss = None
+        if dev.k_scales is not None:
+            kss = torch.zeros((Bn, Hkv, km), dtype=torch.float32, device="cuda")
+            vss = torch.zeros((Bn, Hkv, km), dtype=torch.float32, device="cuda")
+        B.sparsekv_gather(pr, dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales, dev.block_table,
+                          st.indices, st.n_sel, ks, vs, kss, vss)
+        torch.cuda.synchronize()
+        h = HostArrays(inp)
+        opr = oracle_problem(inp, k_max=km)
+        oks, ovs, okss, ovss = O.gather(opr, *h.pools(), h.block_table, _np(st.indices), _np(st.n_sel))
+        nsel = _np(st.n_sel)
+        from sparse_kv_cache_block_amd.inputs import raw_bytes
+        gks, gvs = raw_bytes(ks), raw_bytes(vs)
+        for b in range(Bn):
+            for g in range(Hkv):
+                n = int(nsel[b, 0, g])
+                assert np.array_equal(gks[b, g, :n].view(np.uint8), oks[b, g, :n].view(np.uint8))
+                assert np.array_equal(gvs[b, g, :n].view(np.uint8), ovs[b, g, :n].view(np.uint8))
+                if kss is not None:
+                    assert np.array_equal(_np(kss)[b, g, :n], okss[b, g, :n])
+                    assert np.array_equal(_np(vss)[b, g, :n], ovss[b, g, :n])
+        # attention from the staged copy equals attention straight from the pool
+        out2 = torch.empty_like(st.out)
+        lse2 = torch.empty_like(st.lse)
+        sparse = B.kv_source(B.SKV_SRC_STAGED, ks, vs, kss, vss)
+        window = B.kv_source(B.SKV_SRC_PAGED, dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales,
+                             dev.block_table)
+        B.sparsekv_attend(pr, dev.q, sparse, st.indices, st.n_sel, window, dev.seq_lens, out2, lse2, st.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, st.out) and torch.equal(lse2, st.lse)
+
+
+def test_host_layer_pipeline_matches_single_steps():
+    wl = configs.HOST.scaled(batch=2, context=8192)
+    announce("sparsekv_decode_layers (ping-pong, 4 layers) vs single steps")
+    inp, st = run_step(wl)
+    outs = st.run_layers(4, copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o["indices"], st.indices)
+        assert torch.equal(o["out"], st.out) and torch.equal(o["lse"], st.lse)
+
+
+def test_repeated_calls_reuse_workspace():
+    wl = configs.LLAMA32K.scaled(batch=2, context=4096)
+    announce("repeated decode steps on one workspace")
+    inp, st = run_step(wl)
+    first = st.out.clone()
+    for _ in range(3):
+        st.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first, st.out)
+
+
+# ------------------------------------------------------------ full-size workloads
+@pytest.mark.parametrize("name", ["llama32k", "dual", "ragged", "host"])
+def test_full_size_workload(name):
+    wl = configs.get(name)
+    check_step(wl, gen_device="cuda")
