@@ -19,7 +19,7 @@
 // In the fused decode step the scoring grid is split over workgroups per
 // (sequence, KV head); the last workgroup to finish (device-scope atomic
 // counter, reset by that workgroup) runs the selection over the fp32 scores
-// its siblings left in the workspace.
+// its siblings published to the workspace with device-scope stores.
 #include "skv_device.h"
 #include "skv_internal.h"
 
@@ -167,11 +167,12 @@ __device__ __forceinline__ int n_candidates(int L, int window, int blk) {
 __device__ void select_rows(const float* scores, int64_t t_stride, int nc, int T, int k, int k_max,
                             int32_t* indices, int64_t idx_t_stride, int32_t* n_sel,
                             int64_t nsel_t_stride, float* overlap_out, uint32_t* keys,
-                            int32_t* lds_idx, TopkShared& sh) {
+                            int32_t* lds_idx, TopkShared& sh, bool coherent) {
   int ns[2] = {0, 0};
   for (int t = 0; t < T; ++t) {
     const float* row = scores + t * t_stride;
-    for (int j = threadIdx.x; j < nc; j += kThreads) keys[j] = score_key(row[j]);
+    for (int j = threadIdx.x; j < nc; j += kThreads)
+      keys[j] = score_key(coherent ? fetch_f32(row + j) : row[j]);
     __syncthreads();
     ns[t] = block_select(keys, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
     if (threadIdx.x == 0) n_sel[t * nsel_t_stride] = ns[t];
@@ -271,7 +272,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
         for (int t = 0; t < T; ++t) {
           float val = acc[t];
           if (val == 0.0f) val = 0.0f;  // one zero
-          sc[t * t_stride + r] = (r < nc) ? val : -INFINITY;
+          val = (r < nc) ? val : -INFINITY;
+          if (p.fused_select) publish_f32(sc + t * t_stride + r, val);
+          else sc[t * t_stride + r] = val;
         }
       }
     }
@@ -281,17 +284,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
 
   // ---- last workgroup of (b, g) selects
   __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned* cnt = p.counters + b * p.Hkv + g;
-    const unsigned old = atomicAdd(cnt, 1u);
-    s_last = (old == (unsigned)(nchunks - 1));
-    if (s_last) *cnt = 0u;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, &s_last)) return;
 
   __shared__ TopkShared sh;
   uint32_t* keys = smem + T * D;
@@ -300,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
   select_rows(sc, t_stride, nc, T, k, p.k_max,
               p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max,
               p.n_sel + (int64_t)b * T * p.Hkv + g, p.Hkv,
-              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh);
+              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh, true);
 }
 
 // Stand-alone selection over a caller's score array: one workgroup per (g, b).
@@ -316,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
               p.k_per_seq[b], p.k_max,
               p.indices + ((int64_t)b * p.T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max,
               p.n_sel + (int64_t)b * p.T * p.Hkv + g, p.Hkv,
-              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh);
+              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh, false);
 }
 
 // ------------------------------------------------------------ launchers

@@ -95,4 +95,36 @@ __device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src
 // later reads (LDS operations of a wave complete in order).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// ------------------------------------------------- cross-workgroup hand-off
+// Split results travel between workgroups of one launch through device-scope
+// (agent) atomic stores and loads, which the memory system keeps coherent
+// across the XCDs' separate L2 caches.  A producer waits for its own stores to
+// complete (vmcnt), the workgroup barrier makes that true for every thread,
+// and only then does one thread bump the arrival counter; the last arriver
+// reads the others' values with device-scope loads.  This avoids an
+// agent-scope fence per workgroup, which on this chip writes back and
+// invalidates the whole L2 of the XCD.
+__device__ __forceinline__ void publish_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Called by every thread after its publish_f32 stores; returns true in the
+// workgroup that arrives last among `expected`, after resetting the counter.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, int* flag) {
+  wait_own_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == expected - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 }  // namespace skv

@@ -64,9 +64,10 @@ struct AttnParams {
   const float* wvs;
   const int32_t* window_table;  // block table for a PAGED window
   const int32_t* seq_lens;
-  // split-K layout
-  int n_sparse_splits, n_window_splits, bps, bpw;
-  float* partials;          // [B][Hkv][splits][G][d + 2]
+  // split-K layout: workgroup s of (b, g) owns items [s*items_per_split, ...)
+  // of the concatenated list (sparse slices, then window slices)
+  int n_splits, items_per_split;
+  float* partials;          // [B][Hkv][n_splits][G][d + 2]
   unsigned* counters;       // [B][Hkv]
   float* out;               // [B][Hq][d]
   float* lse;               // [B][Hq] or null
@@ -96,7 +97,7 @@ struct GatherParams {
 struct Plan {
   int max_cand;             // upper bound of candidates per sequence
   int rows_per_chunk, score_chunks;
-  int bps, bpw, n_sparse_splits, n_window_splits;
+  int items_per_split, n_splits;   // attention split-K
   size_t off_score_counters, off_attn_counters, off_scores, off_partials, total_bytes;
 };
 

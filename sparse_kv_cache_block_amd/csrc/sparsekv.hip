@@ -81,6 +81,8 @@ skv_status check_problem(const skv_problem* pr) {
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+constexpr int kAttnTargetWorkgroups = 768;   // ~3 per compute unit on 256 CUs
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -100,22 +102,17 @@ Plan make_plan(const skv_problem& p) {
   if (rows > 1024) rows = 1024;
   pl.rows_per_chunk = rows;
   pl.score_chunks = pl.max_cand > 0 ? (pl.max_cand + rows - 1) / rows : 1;
-  // attention: blocks per split, aiming at ~2048 sparse workgroups
-  int bps = (int)(((int64_t)pairs * p.k_max + 2047) / 2048);
-  bps = round_up(bps < 4 ? 4 : bps, 4);
-  if (bps > 32) bps = 32;
-  pl.bps = bps;
-  pl.n_sparse_splits = (p.k_max + bps - 1) / bps;
+  // attention: items (32-token slices) of the sparse + window list per split,
+  // aiming at about three resident workgroups per compute unit
+  const int sub = blk >= 32 ? blk / 32 : 1;
   const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
-  if (nwb == 0) {
-    pl.bpw = 1;
-    pl.n_window_splits = 0;
-  } else {
-    const int splits = (nwb + bps - 1) / bps;
-    pl.bpw = (nwb + splits - 1) / splits;
-    pl.n_window_splits = splits;
-  }
-  const int total = pl.n_sparse_splits + pl.n_window_splits;
+  const int total_items = (p.k_max + nwb) * sub;
+  int ips = (int)(((int64_t)pairs * total_items + kAttnTargetWorkgroups - 1) / kAttnTargetWorkgroups);
+  if (ips < 8) ips = 8;
+  if (ips > 64) ips = 64;
+  pl.items_per_split = ips;
+  pl.n_splits = (total_items + ips - 1) / ips;
+  const int total = pl.n_splits;
   size_t off = 0;
   pl.off_score_counters = off;
   off = align256(off + (size_t)pairs * 4);
@@ -170,10 +167,8 @@ AttnParams attn_params(const skv_problem& p, const Plan& pl, const void* q, cons
   a.stride_block = p.pool_stride_block;
   a.stride_head = p.pool_stride_head;
   a.seq_lens = seq_lens;
-  a.n_sparse_splits = pl.n_sparse_splits;
-  a.n_window_splits = pl.n_window_splits;
-  a.bps = pl.bps;
-  a.bpw = pl.bpw;
+  a.n_splits = pl.n_splits;
+  a.items_per_split = pl.items_per_split;
   a.partials = reinterpret_cast<float*>(ws + pl.off_partials);
   a.counters = reinterpret_cast<unsigned*>(ws + pl.off_attn_counters);
   a.out = out;
