@@ -24,7 +24,7 @@
 // scale multiplies the logits and the V scale multiplies P.  The next item's
 // K/V loads are issued before the current item's softmax and P V, so each
 // wave keeps one item in flight while it computes.  Online softmax runs in
-// the log2 domain in fp32.  The four waves' partials are combined in LDS;
+// the log2 domain in fp32.  The eight waves' partials are combined in LDS;
 // each workgroup publishes (max, sum, unnormalised O) per head, and the last
 // workgroup of the (sequence, KV head) merges all of them into the fp32
 // output and lse.
@@ -32,6 +32,9 @@
 #include "skv_internal.h"
 
 namespace skv {
+
+constexpr int kAttnWaves = 8;                 // waves per attention workgroup
+constexpr int kAttnThreads = kAttnWaves * kWave;
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -72,10 +75,12 @@ __device__ __forceinline__ ItemDesc describe(const AttnParams& p, int b, int g, 
   const int blk_item = item / C::SUB, sub = item % C::SUB;
   if (blk_item < nsel) {
     const int m = blk_item;
-    const int j = p.indices[((int64_t)b * p.T * p.Hkv + g) * p.k_max + m];
+    const int64_t row = ((int64_t)b * p.T * p.Hkv + g) * p.k_max + m;
+    const int j = p.indices[row];
     d.pos0 = j * BLK + sub * C::TB;
     if (p.sparse_kind == SKV_SRC_PAGED) {
-      const int64_t phys = p.block_table[(int64_t)b * p.max_blocks + j];
+      // physical ids emitted by the selection save the dependent table lookup
+      const int64_t phys = p.phys ? p.phys[row] : p.block_table[(int64_t)b * p.max_blocks + j];
       d.off = phys * p.stride_block + (int64_t)g * p.stride_head;
       if (KV == KV_FP8) {
         d.ks = p.sks[phys * p.Hkv + g];
@@ -111,9 +116,9 @@ __device__ __forceinline__ ItemDesc describe(const AttnParams& p, int b, int g, 
 }
 
 template <int KV, int D, int BLK>
-__global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   using C = AttnCfg<KV, D, BLK>;
-  __shared__ __attribute__((aligned(16))) char smem[kWaves * C::PER_WAVE];
+  __shared__ __attribute__((aligned(16))) char smem[kAttnWaves * C::PER_WAVE];
   __shared__ int s_last;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -136,11 +141,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
   const int first = split * p.items_per_split;
   int count = min(p.items_per_split, total - first);
   if (count < 0) count = 0;
-  const int my_items = count > w ? (count - w + kWaves - 1) / kWaves : 0;  // this wave's items
-
-  // lane j describes this wave's item j (items first + w, first + w + 4, ...)
-  ItemDesc mine{0, 0, 1.f, 1.f};
-  if (lane < my_items) mine = describe<KV, D, BLK>(p, b, g, first + w + kWaves * lane, nsel, ws);
+  const int my_items = count > w ? (count - w + kAttnWaves - 1) / kAttnWaves : 0;  // this wave's items
 
   // ---- query operand: column n holds head n (and head n-G for the low half)
   const int ncols = KV == KV_F32 ? G : 2 * G;
@@ -165,6 +166,10 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
       }
     }
   }
+
+  // lane j describes this wave's item j (items first + w, first + w + kAttnWaves, ...)
+  ItemDesc mine{0, 0, 1.f, 1.f};
+  if (lane < my_items) mine = describe<KV, D, BLK>(p, b, g, first + w + kAttnWaves * lane, nsel, ws);
 
   const char* kbase_s = static_cast<const char*>(p.sk);
   const char* vbase_s = static_cast<const char*>(p.sv);
@@ -255,7 +260,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
         *reinterpret_cast<uint4*>(vt + row * C::VROW + 2 * col) = a;
         *reinterpret_cast<uint4*>(vt + row * C::VROW + 2 * col + 16) = c;
       } else {
-        *reinterpret_cast<uint4*>(vt + row * C::VROW + col) = ok ? vr[i] : make_uint4(0, 0, 0, 0);
+        uint4 val = vr[i];
+        if (partial && !ok) val = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(vt + row * C::VROW + col) = val;
       }
     }
 
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
     wave_lds_sync();
   }
 
-  // ---- combine the four waves in LDS
+  // ---- combine the waves in LDS
   float lsum = l_run;
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
@@ -372,16 +379,16 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
   __syncthreads();
   const int64_t pair = (int64_t)b * p.Hkv + g;
   float* part = p.partials + (pair * n_splits + split) * G * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
+    for (int ww = 0; ww < kAttnWaves; ++ww)
       M = fmaxf(M, reinterpret_cast<const float*>(smem + ww * C::PER_WAVE)[16 * D + h]);
     float O = 0.f, Ls = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
+      for (int ww = 0; ww < kAttnWaves; ++ww) {
         const float* comb = reinterpret_cast<const float*>(smem + ww * C::PER_WAVE);
         const float mw = comb[16 * D + h];
         if (mw == -INFINITY) continue;
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
   float* ll = mm + n_splits * G;                 // [n_splits][G]
   float* wgt = ll + n_splits * G;                // [n_splits][G]
   float* hres = wgt + n_splits * G;              // [G] lse in log2 units
-  for (int i = threadIdx.x; i < n_splits * G; i += kThreads) {
+  for (int i = threadIdx.x; i < n_splits * G; i += kAttnThreads) {
     const int s = i / G, h = i % G;
     mm[i] = fetch_f32(pb + ((int64_t)s * G + h) * (D + 2));
     ll[i] = fetch_f32(pb + ((int64_t)s * G + h) * (D + 2) + 1);
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
     hres[h] = M == -INFINITY ? -INFINITY : M + log2f(Ls);
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
     const int h = idx / D, d = idx % D;
     float acc = 0.f;
     constexpr int SB = 8;
@@ -457,9 +464,9 @@ __global__ __launch_bounds__(kThreads) void attend_kernel(AttnParams p) {
 template <int KV, int D>
 static hipError_t launch_blk(const AttnParams& p, dim3 grid, hipStream_t s) {
   switch (p.blk) {
-    case 16: hipLaunchKernelGGL((attend_kernel<KV, D, 16>), grid, dim3(kThreads), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((attend_kernel<KV, D, 32>), grid, dim3(kThreads), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((attend_kernel<KV, D, 64>), grid, dim3(kThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((attend_kernel<KV, D, 16>), grid, dim3(kAttnThreads), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((attend_kernel<KV, D, 32>), grid, dim3(kAttnThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((attend_kernel<KV, D, 64>), grid, dim3(kAttnThreads), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -27,8 +27,11 @@ namespace skv {
 
 // ------------------------------------------------------------ block scan
 
-// Exclusive prefix sum over the 256 threads of a workgroup.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds4, uint32_t& total) {
+constexpr int kSelThreads = 512;             // threads of the scoring / selection workgroups
+constexpr int kSelWaves = kSelThreads / kWave;
+
+// Exclusive prefix sum over the kSelThreads threads of a workgroup.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_w, uint32_t& total) {
   const int lane = lane_id(), w = wave_id();
   uint32_t x = v;
 #pragma unroll
@@ -36,12 +39,12 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds4, uint32_t& t
     uint32_t y = __shfl_up(x, off, kWave);
     if (lane >= off) x += y;
   }
-  if (lane == kWave - 1) lds4[w] = x;
+  if (lane == kWave - 1) lds_w[w] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    uint32_t t = lds4[i];
+  for (int i = 0; i < kSelWaves; ++i) {
+    uint32_t t = lds_w[i];
     base += (i < w) ? t : 0u;
     tot += t;
   }
@@ -52,15 +55,17 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds4, uint32_t& t
 
 struct TopkShared {
   uint32_t hist[256];
-  uint32_t scan4[kWaves];
+  uint32_t scan_w[kSelWaves];
   uint32_t digit, above, common;
 };
 
 // Select the k largest of keys[0..n) (ties to the lowest index).  Writes the
 // chosen indices in ascending order to out[0..k') and -1 to out[k'..k_max);
 // mirrors them to lds_out when given.  Returns k' = clamp(k, 0, min(n, k_max)).
-__device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32_t* out,
-                            int32_t* lds_out, TopkShared& sh) {
+// Radix select on 8-bit digits, most significant first: after four passes the
+// k'-th largest key is known exactly, with `take_eq` of its copies to keep.
+__device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32_t* out,
+                                            int32_t* lds_out, TopkShared& sh) {
   const int tid = threadIdx.x;
   int kk = k < n ? k : n;
   if (kk > k_max) kk = k_max;  // the output row holds k_max entries
@@ -70,18 +75,18 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32
   if (!take_all && kk > 0) {
     uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kk;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      sh.hist[tid] = 0;
+      if (tid < 256) sh.hist[tid] = 0;
       __syncthreads();
-      for (int j = tid; j < n; j += kThreads) {
+      for (int j = tid; j < n; j += kSelThreads) {
         const uint32_t key = keys[j];
         if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      // thread tid owns digit 255 - tid: the scan gives how many keys lie above it
-      const uint32_t c = sh.hist[255 - tid];
+      // thread tid < 256 owns digit 255 - tid: the scan counts the keys above it
+      const uint32_t c = tid < 256 ? sh.hist[255 - tid] : 0u;
       uint32_t tot;
-      const uint32_t above = block_exclusive_scan(c, sh.scan4, tot);
-      if (above < remaining && above + c >= remaining) {
+      const uint32_t above = block_exclusive_scan(c, sh.scan_w, tot);
+      if (tid < 256 && above < remaining && above + c >= remaining) {
         sh.digit = 255u - tid;
         sh.above = above;
       }
@@ -95,7 +100,7 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32
     take_eq = remaining;
   }
   // Emit in ascending index order: thread tid owns indices [j0, j1).
-  const int per = (n + kThreads - 1) / kThreads;
+  const int per = (n + kSelThreads - 1) / kSelThreads;
   const int j0 = tid * per;
   const int j1 = min(n, j0 + per);
   uint32_t gt = 0, eq = 0;
@@ -106,7 +111,7 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32
       eq += key == thresh;
     }
   uint32_t tot;
-  const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.scan4, tot);
+  const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.scan_w, tot);
   if (take_all) {
     for (int j = j0; j < j1; ++j) {
       out[j] = j;
@@ -131,7 +136,7 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32
     }
   }
   const int nsel = take_all ? n : kk;
-  for (int m = nsel + tid; m < k_max; m += kThreads) {
+  for (int m = nsel + tid; m < k_max; m += kSelThreads) {
     out[m] = -1;
     if (lds_out) lds_out[m] = -1;
   }
@@ -139,11 +144,12 @@ __device__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32
 }
 
 // |a & b| / |a| for two ascending index lists in LDS (1 when a is empty).
-__device__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb, TopkShared& sh) {
+__device__ __forceinline__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb,
+                                              TopkShared& sh) {
   if (threadIdx.x == 0) sh.common = 0;
   __syncthreads();
   uint32_t local = 0;
-  for (int i = threadIdx.x; i < na; i += kThreads) {
+  for (int i = threadIdx.x; i < na; i += kSelThreads) {
     const int x = a[i];
     int lo = 0, hi = nb;
     while (lo < hi) {
@@ -162,38 +168,76 @@ __device__ __forceinline__ int n_candidates(int L, int window, int blk) {
   return (ws + blk - 1) / blk;
 }
 
-// Selection for one (b, g) and every query token, keys read from `scores`
-// (row stride `cols`).  Dynamic LDS layout: keys[max_cand] | idx[2][k_max].
-__device__ void select_rows(const float* scores, int64_t t_stride, int nc, int T, int k, int k_max,
-                            int32_t* indices, int64_t idx_t_stride, int32_t* n_sel,
-                            int64_t nsel_t_stride, float* overlap_out, uint32_t* keys,
-                            int32_t* lds_idx, TopkShared& sh, bool coherent) {
-  int ns[2] = {0, 0};
+// Keys of one token's row from a score array in global memory into LDS.
+__device__ __forceinline__ void load_keys(const float* row, int nc, bool coherent, uint32_t* keys) {
+  constexpr int KB = 8;  // loads in flight per thread
+  for (int j0 = threadIdx.x; j0 < nc; j0 += KB * kSelThreads) {
+    float v[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = j0 + u * kSelThreads;
+      v[u] = j < nc ? (coherent ? fetch_f32(row + j) : row[j]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = j0 + u * kSelThreads;
+      if (j < nc) keys[j] = score_key(v[u]);
+    }
+  }
+}
+
+// Selection for one (b, g) and every query token.  Token t's keys are at
+// keys + t * key_stride (already there when `scores` is null, else loaded
+// from scores + t * t_stride).
+__device__ __forceinline__ void select_rows(const float* scores, int64_t t_stride, bool coherent,
+                                            uint32_t* keys, int key_stride, int nc, int T, int k,
+                                            int k_max, int32_t* indices, int64_t idx_t_stride,
+                                            int32_t* n_sel, int64_t nsel_t_stride, float* overlap_out,
+                                            int32_t* lds_idx, TopkShared& sh) {
+  int ns0 = 0, ns1 = 0;
   for (int t = 0; t < T; ++t) {
-    const float* row = scores + t * t_stride;
-    for (int j = threadIdx.x; j < nc; j += kThreads)
-      keys[j] = score_key(coherent ? fetch_f32(row + j) : row[j]);
-    __syncthreads();
-    ns[t] = block_select(keys, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
-    if (threadIdx.x == 0) n_sel[t * nsel_t_stride] = ns[t];
+    uint32_t* kt = keys + t * key_stride;
+    if (scores) {
+      load_keys(scores + t * t_stride, nc, coherent, kt);
+      __syncthreads();
+    }
+    const int ns = block_select(kt, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
+    if (t == 0) ns0 = ns; else ns1 = ns;
+    if (threadIdx.x == 0) n_sel[t * nsel_t_stride] = ns;
     __syncthreads();
   }
   if (T == 2 && overlap_out) {
-    const float ov = list_overlap(lds_idx, ns[0], lds_idx + k_max, ns[1], sh);
+    const float ov = list_overlap(lds_idx, ns0, lds_idx + k_max, ns1, sh);
     if (threadIdx.x == 0) *overlap_out = ov;
+  }
+}
+
+// Physical block of every selected index (row b of the block table).
+__device__ __forceinline__ void write_phys(const int32_t* lds_idx, int T, int k_max,
+                                           const int32_t* table_row, int32_t* phys,
+                                           int64_t t_stride) {
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k_max; i += kSelThreads) {
+    const int t = i / k_max, m = i % k_max;
+    const int j = lds_idx[i];
+    phys[t * t_stride + m] = j >= 0 ? table_row[j] : -1;
   }
 }
 
 // ------------------------------------------------------------ scoring
 
+// Grid (chunk, g, b).  Modes: stand-alone scoring (scores to global, -inf past
+// the candidates); fused with one chunk per (b, g) (scores go straight to LDS
+// keys and the same workgroup selects); fused with several chunks (scores are
+// published to the workspace and the last chunk to arrive selects).
 template <int D, bool LM_F32>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
+__global__ __launch_bounds__(kSelThreads) void score_kernel(ScoreParams p) {
   constexpr int ES = LM_F32 ? 4 : 2;
-  constexpr int LPR = D * ES / 16;   // lanes per landmark row
-  constexpr int EPL = 16 / ES;       // landmark elements per lane
-  constexpr int RPW = kWave / LPR;   // rows per wave per step
-  constexpr int RPS = RPW * kWaves;  // rows per workgroup per step
-  constexpr int UR = 4;              // steps whose loads are in flight together
+  constexpr int LPR = D * ES / 16;      // lanes per landmark row
+  constexpr int EPL = 16 / ES;          // landmark elements per lane
+  constexpr int RPW = kWave / LPR;      // rows per wave per step
+  constexpr int RPS = RPW * kSelWaves;  // rows per workgroup per step
+  constexpr int UR = 8;                 // steps whose loads are in flight together
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = p.T;
@@ -210,10 +254,32 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     row_begin = c * R;
     row_end = min(p.max_blocks, row_begin + R);
   }
+  const bool in_lds = p.fused_select && p.single_chunk;
 
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   float* qbar = reinterpret_cast<float*>(smem);  // [T][D]
-  for (int i = threadIdx.x; i < T * D; i += kThreads) {
+  uint32_t* keys = smem + T * D;                 // [T][score_cols]
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + T * p.score_cols);
+
+  const int lane = lane_id(), w = wave_id();
+  const int sub = lane % LPR, rw = lane / LPR;
+  const char* lm = static_cast<const char*>(p.landmarks) +
+                   ((int64_t)(b * p.Hkv + g) * p.max_blocks) * D * ES + sub * 16;
+  const int steps = (row_end - row_begin + RPS - 1) / RPS;
+
+  uint4 v[UR];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
+      v[u] = (s0 + u < steps && r < row_end && r < nc)
+                 ? *reinterpret_cast<const uint4*>(lm + (int64_t)r * D * ES)
+                 : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (steps > 0) load_batch(0);   // in flight while the group query is formed
+
+  for (int i = threadIdx.x; i < T * D; i += kSelThreads) {
     const int t = i / D, d = i % D;
     const int64_t base = ((int64_t)(b * T + t) * p.Hq + (int64_t)g * p.G) * D + d;
     float s = 0.f;
@@ -223,30 +289,17 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
     qbar[i] = s;
   }
   __syncthreads();
-
-  const int lane = lane_id(), w = wave_id();
-  const int sub = lane % LPR, rw = lane / LPR;
   float qr[2][EPL];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qr[t][e] = (t < T) ? qbar[t * D + sub * EPL + e] : 0.f;
 
-  const char* lm = static_cast<const char*>(p.landmarks) +
-                   ((int64_t)(b * p.Hkv + g) * p.max_blocks) * D * ES + sub * 16;
   float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
   const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
 
-  const int steps = (row_end - row_begin + RPS - 1) / RPS;
   for (int s0 = 0; s0 < steps; s0 += UR) {
-    uint4 v[UR];
-#pragma unroll
-    for (int u = 0; u < UR; ++u) {
-      const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
-      v[u] = (s0 + u < steps && r < row_end && r < nc)
-                 ? *reinterpret_cast<const uint4*>(lm + (int64_t)r * D * ES)
-                 : make_uint4(0, 0, 0, 0);
-    }
+    if (s0 > 0) load_batch(s0);
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
       const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
@@ -258,23 +311,26 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
         x[0] = bf16_lo(v[u].x); x[1] = bf16_hi(v[u].x); x[2] = bf16_lo(v[u].y); x[3] = bf16_hi(v[u].y);
         x[4] = bf16_lo(v[u].z); x[5] = bf16_hi(v[u].z); x[6] = bf16_lo(v[u].w); x[7] = bf16_hi(v[u].w);
       }
-      float acc[2];
+      float acc[2] = {0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float a = 0.f;
+      for (int e = 0; e < EPL; ++e) acc[0] = fmaf(qr[0][e], x[e], acc[0]);
+      acc[0] = group_sum<LPR>(acc[0]);
+      if (T == 2) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) a = fmaf(qr[t][e], x[e], a);
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) a += shfl_xor_f(a, off);
-        acc[t] = a;
+        for (int e = 0; e < EPL; ++e) acc[1] = fmaf(qr[1][e], x[e], acc[1]);
+        acc[1] = group_sum<LPR>(acc[1]);
       }
       if (sub == 0 && s0 + u < steps && r < row_end) {
         for (int t = 0; t < T; ++t) {
           float val = acc[t];
           if (val == 0.0f) val = 0.0f;  // one zero
-          val = (r < nc) ? val : -INFINITY;
-          if (p.fused_select) publish_f32(sc + t * t_stride + r, val);
-          else sc[t * t_stride + r] = val;
+          if (in_lds) {
+            keys[t * p.score_cols + r] = score_key(val);
+          } else {
+            val = (r < nc) ? val : -INFINITY;
+            if (p.fused_select) publish_f32(sc + t * t_stride + r, val);
+            else sc[t * t_stride + r] = val;
+          }
         }
       }
     }
@@ -282,22 +338,29 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreParams p) {
 
   if (!p.fused_select) return;
 
-  // ---- last workgroup of (b, g) selects
-  __shared__ int s_last;
-  if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, &s_last)) return;
-
   __shared__ TopkShared sh;
-  uint32_t* keys = smem + T * D;
-  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + p.score_cols);
   const int k = p.k_per_seq[b];
-  select_rows(sc, t_stride, nc, T, k, p.k_max,
-              p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max,
-              p.n_sel + (int64_t)b * T * p.Hkv + g, p.Hkv,
-              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh, true);
+  int32_t* idx_out = p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max;
+  int32_t* nsel_out = p.n_sel + (int64_t)b * T * p.Hkv + g;
+  float* ov_out = p.overlap ? p.overlap + b * p.Hkv + g : nullptr;
+  if (in_lds) {
+    __syncthreads();
+    select_rows(nullptr, 0, false, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
+                (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
+  } else {
+    // ---- several chunks: the last one of (b, g) to arrive selects
+    __shared__ int s_last;
+    if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, &s_last)) return;
+    select_rows(sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
+                (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
+  }
+  if (p.phys)
+    write_phys(lds_idx, T, p.k_max, p.block_table + (int64_t)b * p.max_blocks,
+               p.phys + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max);
 }
 
 // Stand-alone selection over a caller's score array: one workgroup per (g, b).
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
+__global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkParams p) {
   const int g = blockIdx.x, b = blockIdx.y;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   __shared__ TopkShared sh;
@@ -305,11 +368,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkParams p) {
   uint32_t* keys = smem;
   int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + p.max_blocks);
   const int64_t t_stride = (int64_t)p.Hkv * p.max_blocks;
-  select_rows(p.scores + ((int64_t)b * p.T * p.Hkv + g) * p.max_blocks, t_stride, nc, p.T,
-              p.k_per_seq[b], p.k_max,
-              p.indices + ((int64_t)b * p.T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max,
-              p.n_sel + (int64_t)b * p.T * p.Hkv + g, p.Hkv,
-              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, keys, lds_idx, sh, false);
+  select_rows(p.scores + ((int64_t)b * p.T * p.Hkv + g) * p.max_blocks, t_stride, false, keys, 0, nc,
+              p.T, p.k_per_seq[b], p.k_max, p.indices + ((int64_t)b * p.T * p.Hkv + g) * p.k_max,
+              (int64_t)p.Hkv * p.k_max, p.n_sel + (int64_t)b * p.T * p.Hkv + g, p.Hkv,
+              p.overlap ? p.overlap + b * p.Hkv + g : nullptr, lds_idx, sh);
 }
 
 // ------------------------------------------------------------ launchers
@@ -319,20 +381,20 @@ size_t topk_lds_bytes(int max_cand) { return (size_t)max_cand * 4; }
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s) {
   const dim3 grid(chunks, p.Hkv, p.B);
   size_t lds = (size_t)p.T * p.D * 4;
-  if (p.fused_select) lds += topk_lds_bytes(p.score_cols) + (size_t)2 * p.k_max * 4;
+  if (p.fused_select) lds += (size_t)p.T * topk_lds_bytes(p.score_cols) + (size_t)2 * p.k_max * 4;
   if (p.D == 128) {
-    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<128, true>), grid, dim3(kThreads), lds, s, p);
-    else hipLaunchKernelGGL((score_kernel<128, false>), grid, dim3(kThreads), lds, s, p);
+    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<128, true>), grid, dim3(kSelThreads), lds, s, p);
+    else hipLaunchKernelGGL((score_kernel<128, false>), grid, dim3(kSelThreads), lds, s, p);
   } else {
-    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<64, true>), grid, dim3(kThreads), lds, s, p);
-    else hipLaunchKernelGGL((score_kernel<64, false>), grid, dim3(kThreads), lds, s, p);
+    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<64, true>), grid, dim3(kSelThreads), lds, s, p);
+    else hipLaunchKernelGGL((score_kernel<64, false>), grid, dim3(kSelThreads), lds, s, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t s) {
   const size_t lds = topk_lds_bytes(p.max_blocks) + (size_t)2 * p.k_max * 4;
-  hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL(topk_kernel, dim3(p.Hkv, p.B), dim3(kSelThreads), lds, s, p);
   return hipGetLastError();
 }
 

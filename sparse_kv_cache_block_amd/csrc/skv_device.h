@@ -89,6 +89,30 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Data-parallel-primitive (DPP) lane moves inside a 16-lane row: plain VALU
+// operands, no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N in {4, 8, 16, 32, 64}); every lane of
+// a group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float a) {
+  a += dpp_f<kDppQuadXor1>(a);
+  a += dpp_f<kDppQuadXor2>(a);
+  if constexpr (N >= 8) a += dpp_f<kDppRowHalfMirror>(a);
+  if constexpr (N >= 16) a += dpp_f<kDppRowMirror>(a);
+  if constexpr (N >= 32) a += __shfl_xor(a, 16, kWave);
+  if constexpr (N >= 64) a += __shfl_xor(a, 32, kWave);
+  return a;
+}
 __device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, kWave); }
 
 // Compiler and LDS ordering point between one wave's LDS writes and its own

@@ -20,7 +20,8 @@ struct ScoreParams {
   int B, T, Hq, Hkv, G, D, blk, max_blocks, window;
   int q_f32, lm_f32;        // 1 when q / landmarks are fp32, else bf16
   int rows_per_chunk;
-  int fused_select;         // 1: last-arriving workgroup of (b, g) runs the top-k
+  int fused_select;         // 1: the top-k runs in the scoring launch
+  int single_chunk;         // fused: one workgroup per (b, g) scores into LDS and selects
   // fused selection outputs
   const int32_t* k_per_seq;
   int32_t* indices;         // [B][T][Hkv][k_max]
@@ -28,6 +29,8 @@ struct ScoreParams {
   float* overlap;           // [B][Hkv] or null
   int k_max;
   unsigned* counters;       // [B][Hkv], zero between calls
+  const int32_t* block_table;  // when set, the selection also writes
+  int32_t* phys;               // phys[b][t][g][m] = block_table[b][indices[b][t][g][m]]
 };
 
 struct TopkParams {
@@ -55,6 +58,7 @@ struct AttnParams {
   const int32_t* block_table;
   int64_t stride_block, stride_head;  // pool element strides
   const int32_t* indices;   // [B][T][Hkv][k_max] (token 0 rows used)
+  const int32_t* phys;      // same layout: physical block of each index, or null
   const int32_t* n_sel;     // [B][T][Hkv]
   // window part
   int window_kind;          // SKV_SRC_PAGED or SKV_SRC_WINDOW
@@ -98,7 +102,7 @@ struct Plan {
   int max_cand;             // upper bound of candidates per sequence
   int rows_per_chunk, score_chunks;
   int items_per_split, n_splits;   // attention split-K
-  size_t off_score_counters, off_attn_counters, off_scores, off_partials, total_bytes;
+  size_t off_score_counters, off_attn_counters, off_scores, off_partials, off_phys, total_bytes;
 };
 
 Plan make_plan(const skv_problem& pr);

@@ -82,7 +82,12 @@ skv_status check_problem(const skv_problem* pr) {
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-constexpr int kAttnTargetWorkgroups = 768;   // ~3 per compute unit on 256 CUs
+#ifndef SKV_ATTN_TARGET_WGS
+#define SKV_ATTN_TARGET_WGS 256
+#endif
+constexpr int kAttnTargetWorkgroups = SKV_ATTN_TARGET_WGS;   // one 8-wave workgroup per CU
+constexpr int kScoreSinglePairs = 128;       // from this many pairs on, one scoring workgroup per pair
+constexpr int kScoreTargetWorkgroups = 512;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -94,22 +99,26 @@ Plan make_plan(const skv_problem& p) {
   pl.max_cand = p.max_blocks_per_seq - p.window / blk;
   if (pl.max_cand < 0) pl.max_cand = 0;
   const int pairs = p.batch * p.n_kv_heads;
-  // scoring: rows per workgroup chunk, aiming at ~2048 workgroups
+  // scoring: with many (sequence, KV head) pairs one workgroup scores all of a
+  // pair's candidates into LDS and selects in place; with few pairs the rows
+  // are split over about kScoreTargetWorkgroups workgroups
   const int lm_es = p.landmark_dtype == SKV_F32 ? 4 : 2;
-  const int rps = 4 * (64 / (D * lm_es / 16));
-  int rows = (int)(((int64_t)pl.max_cand * pairs + 2047) / 2048);
-  rows = round_up(rows < 64 ? 64 : rows, rps);
-  if (rows > 1024) rows = 1024;
-  pl.rows_per_chunk = rows;
-  pl.score_chunks = pl.max_cand > 0 ? (pl.max_cand + rows - 1) / rows : 1;
+  const int rps = 8 * (64 / (D * lm_es / 16));   // rows per 512-thread step
+  if (pairs >= kScoreSinglePairs || pl.max_cand <= rps) {
+    pl.rows_per_chunk = round_up(pl.max_cand > 0 ? pl.max_cand : 1, rps);
+  } else {
+    const int per_pair = (kScoreTargetWorkgroups + pairs - 1) / pairs;
+    pl.rows_per_chunk = round_up((pl.max_cand + per_pair - 1) / per_pair, rps);
+  }
+  pl.score_chunks = pl.max_cand > 0 ? (pl.max_cand + pl.rows_per_chunk - 1) / pl.rows_per_chunk : 1;
   // attention: items (32-token slices) of the sparse + window list per split,
   // aiming at about three resident workgroups per compute unit
   const int sub = blk >= 32 ? blk / 32 : 1;
   const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
   const int total_items = (p.k_max + nwb) * sub;
   int ips = (int)(((int64_t)pairs * total_items + kAttnTargetWorkgroups - 1) / kAttnTargetWorkgroups);
-  if (ips < 8) ips = 8;
-  if (ips > 64) ips = 64;
+  if (ips < 16) ips = 16;
+  if (ips > 128) ips = 128;
   pl.items_per_split = ips;
   pl.n_splits = (total_items + ips - 1) / ips;
   const int total = pl.n_splits;
@@ -122,6 +131,8 @@ Plan make_plan(const skv_problem& p) {
   off = align256(off + (size_t)pairs * p.n_q_tokens * (pl.max_cand > 0 ? pl.max_cand : 1) * 4);
   pl.off_partials = off;
   off = align256(off + (size_t)pairs * total * G * (D + 2) * 4);
+  pl.off_phys = off;
+  off = align256(off + (size_t)pairs * p.n_q_tokens * p.k_max * 4);
   pl.total_bytes = off;
   return pl;
 }
@@ -230,6 +241,9 @@ skv_status enqueue_score_select(const skv_problem& p, const Plan& pl, const skv_
   sp.score_cols = pl.max_cand > 0 ? pl.max_cand : 1;
   sp.rows_per_chunk = pl.rows_per_chunk;
   sp.fused_select = 1;
+  sp.single_chunk = pl.score_chunks == 1;
+  sp.block_table = in.block_table;
+  sp.phys = reinterpret_cast<int32_t*>(ws + pl.off_phys);
   sp.k_per_seq = in.k_per_seq;
   sp.indices = out.indices;
   sp.n_sel = out.n_sel;
@@ -267,6 +281,7 @@ skv_status enqueue_attend_paged(const skv_problem& p, const Plan& pl, const skv_
   SKV_TRY(set_source(p, a, &win, false));
   a.indices = out.indices;
   a.n_sel = out.n_sel;
+  a.phys = reinterpret_cast<const int32_t*>(ws + pl.off_phys);
   SKV_TRY_HIP(launch_attend(a, s), "attention launch");
   return SKV_OK;
 }
@@ -381,8 +396,8 @@ skv_status sparsekv_score(const skv_problem* pr, const void* q, const void* land
   sp.scores = scores;
   sp.score_cols = p.max_blocks_per_seq;
   const int lm_es = p.landmark_dtype == SKV_F32 ? 4 : 2;
-  const int rps = 4 * (64 / (p.head_dim * lm_es / 16));
-  sp.rows_per_chunk = rps * 16;
+  const int rps = 8 * (64 / (p.head_dim * lm_es / 16));
+  sp.rows_per_chunk = rps * 8;
   sp.fused_select = 0;
   const int chunks = (p.max_blocks_per_seq + sp.rows_per_chunk - 1) / sp.rows_per_chunk;
   SKV_TRY_HIP(launch_score(sp, chunks, as_stream(stream)), "score launch");
