@@ -18,14 +18,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", os.path.join(HERE, "..", "include")]
 
 
-def sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def sources(src_dir: str = CSRC) -> list[str]:
+    return sorted(glob.glob(os.path.join(src_dir, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD_DIR) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD_DIR,
+          src_dir: str = CSRC) -> str:
     """Compile every HIP source and link the shared library; always rebuilds."""
     os.makedirs(build_dir, exist_ok=True)
-    srcs = sources()
+    srcs = sources(src_dir)
 
     def compile_one(src: str) -> str:
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")

@@ -202,10 +202,10 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
     for (int tile = 0; tile < C::NT; ++tile) {
       const char* krow = kb + (16 * tile + n) * (D * C::ES) + 16 * kg;
 #pragma unroll
-      for (int q = 0; q < C::GRAN; ++q) kr[tile][q] = *reinterpret_cast<const uint4*>(krow + 64 * q);
+      for (int q = 0; q < C::GRAN; ++q) kr[tile][q] = load_stream16(krow + 64 * q);
     }
 #pragma unroll
-    for (int i = 0; i < C::NV; ++i) vr[i] = *reinterpret_cast<const uint4*>(vb + 16 * (lane + kWave * i));
+    for (int i = 0; i < C::NV; ++i) vr[i] = load_stream16(vb + 16 * (lane + kWave * i));
   };
 
   if (my_items > 0) load_item(0);

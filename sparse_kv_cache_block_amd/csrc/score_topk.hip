@@ -30,43 +30,54 @@ namespace skv {
 constexpr int kSelThreads = 512;             // threads of the scoring / selection workgroups
 constexpr int kSelWaves = kSelThreads / kWave;
 
-// Exclusive prefix sum over the kSelThreads threads of a workgroup.
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum over the kSelThreads threads of a workgroup (one barrier;
+// the caller alternates `lds_w` between two buffers on consecutive calls).
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_w, uint32_t& total) {
   const int lane = lane_id(), w = wave_id();
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == kWave - 1) lds_w[w] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
-    uint32_t t = lds_w[i];
+    const uint32_t t = lds_w[i];
     base += (i < w) ? t : 0u;
     tot += t;
   }
-  __syncthreads();
   total = tot;
   return base + x - v;
 }
 
 struct TopkShared {
-  uint32_t hist[256];
-  uint32_t scan_w[kSelWaves];
+  uint32_t hist[2][256];
+  uint32_t scan_w[2][kSelWaves];
   uint32_t digit, above, common;
 };
 
 // Select the k largest of keys[0..n) (ties to the lowest index).  Writes the
 // chosen indices in ascending order to out[0..k') and -1 to out[k'..k_max);
 // mirrors them to lds_out when given.  Returns k' = clamp(k, 0, min(n, k_max)).
-// Radix select on 8-bit digits, most significant first: after four passes the
-// k'-th largest key is known exactly, with `take_eq` of its copies to keep.
+//
+// Radix select on 8-bit digits, most significant first: each pass builds the
+// histogram of the digit among the keys that match the known prefix, one wave
+// finds the digit holding the k'-th largest key, and after four passes that
+// key T is known exactly.  Keys above T are all kept; keys equal to T are kept
+// in ascending index order until k' are chosen.
 __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32_t* out,
                                             int32_t* lds_out, TopkShared& sh) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   int kk = k < n ? k : n;
   if (kk > k_max) kk = k_max;  // the output row holds k_max entries
   if (kk < 0) kk = 0;
@@ -74,27 +85,41 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
   uint32_t thresh = 0, take_eq = 0;
   if (!take_all && kk > 0) {
     uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kk;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) sh.hist[tid] = 0;
-      __syncthreads();
+    if (tid < 256) sh.hist[0][tid] = 0;
+    __syncthreads();
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      uint32_t* hist = sh.hist[pass & 1];
       for (int j = tid; j < n; j += kSelThreads) {
         const uint32_t key = keys[j];
-        if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      // thread tid < 256 owns digit 255 - tid: the scan counts the keys above it
-      const uint32_t c = tid < 256 ? sh.hist[255 - tid] : 0u;
-      uint32_t tot;
-      const uint32_t above = block_exclusive_scan(c, sh.scan_w, tot);
-      if (tid < 256 && above < remaining && above + c >= remaining) {
-        sh.digit = 255u - tid;
-        sh.above = above;
+      if (w == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending)
+        uint32_t c[4], lsum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[i] = hist[255 - 4 * lane - i];
+          lsum += c[i];
+        }
+        uint32_t above = wave_inclusive_scan(lsum) - lsum;  // keys in higher digits
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (above < remaining && above + c[i] >= remaining) {
+            sh.digit = 255u - 4 * lane - i;
+            sh.above = above;
+          }
+          above += c[i];
+        }
+      } else if (w == 1) {
+        // meanwhile wave 1 clears the other histogram for the next pass
+        for (int t = lane; t < 256; t += kWave) sh.hist[(pass + 1) & 1][t] = 0;
       }
       __syncthreads();
       prefix |= sh.digit << shift;
       pmask |= 255u << shift;
       remaining -= sh.above;
-      __syncthreads();
     }
     thresh = prefix;
     take_eq = remaining;
@@ -111,7 +136,7 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
       eq += key == thresh;
     }
   uint32_t tot;
-  const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.scan_w, tot);
+  const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh.scan_w[0], tot);
   if (take_all) {
     for (int j = j0; j < j1; ++j) {
       out[j] = j;
@@ -140,6 +165,7 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
     out[m] = -1;
     if (lds_out) lds_out[m] = -1;
   }
+  __syncthreads();  // scan buffer and lds_out are reused by the caller
   return nsel;
 }
 
@@ -237,7 +263,10 @@ __global__ __launch_bounds__(kSelThreads) void score_kernel(ScoreParams p) {
   constexpr int EPL = 16 / ES;          // landmark elements per lane
   constexpr int RPW = kWave / LPR;      // rows per wave per step
   constexpr int RPS = RPW * kSelWaves;  // rows per workgroup per step
-  constexpr int UR = 8;                 // steps whose loads are in flight together
+#ifndef SKV_SCORE_UR
+#define SKV_SCORE_UR 8
+#endif
+  constexpr int UR = SKV_SCORE_UR;      // steps whose loads are in flight together
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int T = p.T;
@@ -273,7 +302,7 @@ __global__ __launch_bounds__(kSelThreads) void score_kernel(ScoreParams p) {
     for (int u = 0; u < UR; ++u) {
       const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
       v[u] = (s0 + u < steps && r < row_end && r < nc)
-                 ? *reinterpret_cast<const uint4*>(lm + (int64_t)r * D * ES)
+                 ? load_stream16(lm + (int64_t)r * D * ES)
                  : make_uint4(0, 0, 0, 0);
     }
   };

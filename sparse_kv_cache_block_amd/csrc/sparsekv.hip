@@ -87,7 +87,7 @@ int round_up(int x, int m) { return (x + m - 1) / m * m; }
 #endif
 constexpr int kAttnTargetWorkgroups = SKV_ATTN_TARGET_WGS;   // one 8-wave workgroup per CU
 constexpr int kScoreSinglePairs = 128;       // from this many pairs on, one scoring workgroup per pair
-constexpr int kScoreTargetWorkgroups = 512;
+constexpr int kScoreTargetWorkgroups = 256;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -397,7 +397,10 @@ skv_status sparsekv_score(const skv_problem* pr, const void* q, const void* land
   sp.score_cols = p.max_blocks_per_seq;
   const int lm_es = p.landmark_dtype == SKV_F32 ? 4 : 2;
   const int rps = 8 * (64 / (p.head_dim * lm_es / 16));
-  sp.rows_per_chunk = rps * 8;
+#ifndef SKV_SCORE_STEPS
+#define SKV_SCORE_STEPS 16
+#endif
+  sp.rows_per_chunk = rps * SKV_SCORE_STEPS;
   sp.fused_select = 0;
   const int chunks = (p.max_blocks_per_seq + sp.rows_per_chunk - 1) / sp.rows_per_chunk;
   SKV_TRY_HIP(launch_score(sp, chunks, as_stream(stream)), "score launch");
