@@ -49,6 +49,47 @@ def attention_bytes(wl, seq_lens, nsel_real) -> int:
     return total
 
 
+KERNEL_SOURCES = ("attend.hip", "skv_device.h", "skv_internal.h")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the attention kernel's sources (counter results go stale when it changes)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_kv_cache_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """Per-launch HBM bytes of the attention kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"attend_kernel_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    if "```json" not in text:
+        return None
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec
+
+
+def copy_probe(mib: int, reps: int) -> int:
+    """A plain device-to-device copy of known size (counter calibration)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps}))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -59,7 +100,11 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, max(1, args.steps))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -161,9 +206,13 @@ def main() -> int:
     roofline = None
     if attn_ms:
         achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+        rec = recorded_traffic(wl.name)
+        traffic = None
+        if rec is not None:
+            traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
         roofline = {"bound": "hbm", "kernel": "attend_kernel", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": None, "bytes_per_launch": int(attn_bytes),
+                    "traffic": traffic, "bytes_per_launch": int(attn_bytes),
                     "us_per_launch": round(attn_ms * 1e3, 2)}
 
     # ---- CPU oracle on a bounded sample of instance 0

@@ -10,9 +10,10 @@
  *            article, section 2: per-head sparse selection; DualDecoder
  *            ledger: a sparse KV budget);
  *   gather   copy the selected (block, head) chunks into a dense staging
- *            buffer (PulseInfer section 2: gather-scatter I/O engine that
- *            coalesces fragmented transfers; DualDecoder Fig. 19: contiguous
- *            block fetch plus a GPU reorder; Fig. 11: two-layer ping-pong
+ *            buffer (PulseInfer article, section 2: an I/O engine that gathers
+ *            the scattered selected entries and merges small transfers into
+ *            large ones; DualDecoder Fig. 19: whole blocks fetched contiguously
+ *            and reordered by GPU kernels; Fig. 11: two-layer ping-pong
  *            staging buffer);
  *   attend   split-K attention over the selected blocks plus dense attention
  *            over the recent window, the partial results fused by

@@ -1,8 +1,9 @@
 // attend.hip -- split-K decode attention over the selected blocks plus the
 // recent window, fused by log-sum-exp, for gfx950.
 //
-// Method (Beyond abstract: dense attention over the recent window and per-head
-// sparse attention over salient KV, combined by a log-sum-exp scheme).  For
+// Method (Beyond abstract: the recent window is attended densely on the GPU,
+// the important older entries sparsely per head, and the two results are
+// merged through their log-sum-exp).  For
 // one (sequence, KV head) the work is a list of items -- 32-token slices of
 // the selected blocks (positions before the window start), then slices of the
 // window blocks (positions in the window) -- and each workgroup of the grid
