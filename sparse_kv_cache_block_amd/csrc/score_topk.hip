@@ -256,7 +256,7 @@ __device__ __forceinline__ void write_phys(const int32_t* lds_idx, int T, int k_
 // the candidates); fused with one chunk per (b, g) (scores go straight to LDS
 // keys and the same workgroup selects); fused with several chunks (scores are
 // published to the workspace and the last chunk to arrive selects).
-template <int D, bool LM_F32>
+template <int D, bool LM_F32, bool Q_F32>
 __global__ __launch_bounds__(kSelThreads) void score_kernel(ScoreParams p) {
   constexpr int ES = LM_F32 ? 4 : 2;
   constexpr int LPR = D * ES / 16;      // lanes per landmark row
@@ -296,28 +296,48 @@ __global__ __launch_bounds__(kSelThreads) void score_kernel(ScoreParams p) {
                    ((int64_t)(b * p.Hkv + g) * p.max_blocks) * D * ES + sub * 16;
   const int steps = (row_end - row_begin + RPS - 1) / RPS;
 
+  // Rows past the range are loaded from the last valid row (and ignored), so
+  // the loads carry no branches and all of a batch is in flight together.
+  const int last_row = max(row_begin, min(row_end, nc) - 1);
   uint4 v[UR];
   auto load_batch = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
-      const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
-      v[u] = (s0 + u < steps && r < row_end && r < nc)
-                 ? load_stream16(lm + (int64_t)r * D * ES)
-                 : make_uint4(0, 0, 0, 0);
+      const int r = min(row_begin + (s0 + u) * RPS + w * RPW + rw, last_row);
+      v[u] = load_stream16(lm + (int64_t)r * D * ES);
     }
   };
-  if (steps > 0) load_batch(0);   // in flight while the group query is formed
+  const bool any_rows = row_end > row_begin && nc > 0;
 
-  for (int i = threadIdx.x; i < T * D; i += kSelThreads) {
-    const int t = i / D, d = i % D;
+  // group-summed query: its G loads per element are issued first (they are
+  // few), then the first landmark batch, so waiting for the query leaves the
+  // landmark loads in flight
+  const int qi = threadIdx.x;                 // T * D <= 256 < kSelThreads
+  const bool q_owner = qi < T * D;
+  uint32_t qraw[8];
+  {
+    const int t = q_owner ? qi / D : 0, d = q_owner ? qi % D : 0;
     const int64_t base = ((int64_t)(b * T + t) * p.Hq + (int64_t)g * p.G) * D + d;
-    float s = 0.f;
-    for (int h = 0; h < p.G; ++h)
-      s += p.q_f32 ? static_cast<const float*>(p.q)[base + (int64_t)h * D]
-                   : bf16_to_f32(static_cast<const uint16_t*>(p.q)[base + (int64_t)h * D]);
-    qbar[i] = s;
+    if constexpr (Q_F32) {
+      const uint32_t* qp = static_cast<const uint32_t*>(p.q) + base;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) qraw[h] = qp[(int64_t)min(h, p.G - 1) * D];
+    } else {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + base;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) qraw[h] = qp[(int64_t)min(h, p.G - 1) * D];
+    }
   }
-  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);   // q loads issue first: waiting on them leaves the batch in flight
+  load_batch(0);   // always in bounds (clamped rows); results are ignored without rows
+  if (q_owner) {
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      sum += h < p.G ? (Q_F32 ? __uint_as_float(qraw[h]) : __uint_as_float(qraw[h] << 16)) : 0.f;
+    qbar[qi] = sum;
+  }
+  lds_barrier();
   float qr[2][EPL];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
@@ -327,7 +347,7 @@ __global__ __launch_bounds__(kSelThreads) void score_kernel(ScoreParams p) {
   float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
   const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
 
-  for (int s0 = 0; s0 < steps; s0 += UR) {
+  for (int s0 = 0; s0 < steps && any_rows; s0 += UR) {
     if (s0 > 0) load_batch(s0);
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
@@ -411,13 +431,20 @@ hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s) {
   const dim3 grid(chunks, p.Hkv, p.B);
   size_t lds = (size_t)p.T * p.D * 4;
   if (p.fused_select) lds += (size_t)p.T * topk_lds_bytes(p.score_cols) + (size_t)2 * p.k_max * 4;
-  if (p.D == 128) {
-    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<128, true>), grid, dim3(kSelThreads), lds, s, p);
-    else hipLaunchKernelGGL((score_kernel<128, false>), grid, dim3(kSelThreads), lds, s, p);
-  } else {
-    if (p.lm_f32) hipLaunchKernelGGL((score_kernel<64, true>), grid, dim3(kSelThreads), lds, s, p);
-    else hipLaunchKernelGGL((score_kernel<64, false>), grid, dim3(kSelThreads), lds, s, p);
+#define SKV_SCORE_LAUNCH(D_, LMF, QF) \
+  hipLaunchKernelGGL((score_kernel<D_, LMF, QF>), grid, dim3(kSelThreads), lds, s, p)
+  const int sel = (p.D == 128 ? 4 : 0) + (p.lm_f32 ? 2 : 0) + (p.q_f32 ? 1 : 0);
+  switch (sel) {
+    case 0: SKV_SCORE_LAUNCH(64, false, false); break;
+    case 1: SKV_SCORE_LAUNCH(64, false, true); break;
+    case 2: SKV_SCORE_LAUNCH(64, true, false); break;
+    case 3: SKV_SCORE_LAUNCH(64, true, true); break;
+    case 4: SKV_SCORE_LAUNCH(128, false, false); break;
+    case 5: SKV_SCORE_LAUNCH(128, false, true); break;
+    case 6: SKV_SCORE_LAUNCH(128, true, false); break;
+    default: SKV_SCORE_LAUNCH(128, true, true); break;
   }
+#undef SKV_SCORE_LAUNCH
   return hipGetLastError();
 }
 

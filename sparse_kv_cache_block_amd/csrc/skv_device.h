@@ -127,6 +127,16 @@ __device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src
 // later reads (LDS operations of a wave complete in order).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS traffic,
+// not for its global loads, so loads issued before it stay in flight.
+// The scheduling barrier keeps the compiler from hoisting work that consumes
+// those loads above it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ------------------------------------------------- cross-workgroup hand-off
 // Split results travel between workgroups of one launch through device-scope
 // (agent) atomic stores and loads, which the memory system keeps coherent
