@@ -1,0 +1,513 @@
+// attend_dev.h -- device code of split-K decode attention over the selected
+// blocks plus the recent window, fused by log-sum-exp, for gfx950; shared by
+// the stand-alone attention kernel and the single-launch decode step.
+//
+// Method (Beyond abstract: the recent window is attended densely on the GPU,
+// the important older entries sparsely per head, and the two results are
+// merged through their log-sum-exp).  For one (sequence, KV head) the work is
+// a list of items -- 32-token slices of the selected blocks (positions before
+// the window start), then slices of the window blocks (positions in the
+// window) -- and each workgroup owns one contiguous range of that list
+// (split-K).  Sparse and window items keep separate position masks, so the
+// sparse and window parts stay disjoint and every partial is an exact softmax
+// partial of its own position set; merging all of them by log-sum-exp is the
+// sparse/window fusion itself.
+//
+// Per item a wave computes, for the G query heads of the group,
+//   S^T = K Q^T    with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 columns);
+// the 16 columns hold the G heads twice (once for fp32), so the C layout
+// leaves lane (column n, row group j) with the logits of tokens 4j..4j+3 --
+// exactly the A-operand layout of the P V product.  Columns G..2G-1 carry the
+// low half of a hi/lo bf16 split of P, so O = P_hi V + P_lo V keeps P to about
+// 2^-17 relative accuracy with one MFMA per 32 tokens.  K rows are read with
+// 16-byte loads straight into the MFMA layout (one 64-byte run of a row per
+// instruction); V goes through LDS and comes back token-major with
+// ds_read_b64_tr_b16.  fp8 e4m3fn data are decoded to bf16 exactly; the K
+// scale multiplies the logits and the V scale multiplies P.  The next item's
+// K/V loads are issued before the current item's softmax and P V, so each
+// wave keeps one item in flight while it computes.  Online softmax runs in
+// the log2 domain in fp32.  The waves' partials are combined in LDS; each
+// workgroup publishes (max, sum, unnormalised O) per head, and the last
+// workgroup of the (sequence, KV head) merges all of them into the fp32
+// output and lse.
+#pragma once
+
+#include "skv_device.h"
+#include "skv_internal.h"
+
+namespace skv {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int KV, int D, int BLK>
+struct AttnCfg {
+  static constexpr int ES = KV == KV_F32 ? 4 : (KV == KV_BF16 ? 2 : 1);
+  static constexpr int TB = BLK < 32 ? BLK : 32;        // tokens per item
+  static constexpr int SUB = BLK / TB;                   // items per block
+  static constexpr int NT = TB / 16;                     // QK tiles per item
+  static constexpr int DT = D / 16;                      // PV output tiles
+  static constexpr int GRAN = D * ES / 64;               // 16-byte K granules per lane per row
+  static constexpr int KS = KV == KV_F32 ? D / 4 : D / 32;  // QK k-steps
+  static constexpr int VE = KV == KV_F32 ? 4 : 2;        // LDS element bytes
+  static constexpr int VROW = D * VE + 16;               // padded LDS row bytes
+  static constexpr int VTILE = TB * VROW;
+  static constexpr int COMB = 16 * D * 4 + 2 * 16 * 4;   // combine region: O rows + m + l
+  static constexpr int PER_WAVE = VTILE > COMB ? VTILE : COMB;
+  static constexpr int ITEM_BYTES = TB * D * ES;         // bytes of one item's K (or V)
+  static constexpr int NV = ITEM_BYTES / (kWave * 16);   // 16-byte V loads per lane
+};
+
+// Descriptor of one item, held by one lane of the wave that processes it.
+struct ItemDesc {
+  int64_t off;    // element offset of the item's first row in its K/V arrays
+  int pos0;       // sequence position of the item's row 0; bit 31 marks a window item
+  float ks, vs;   // fp8 scales
+};
+
+// Slice `sub` of the m-th selected block of (b, g), block id j.  A paged
+// source reads physical block `phys` (negative: look it up in the block
+// table); a staged source reads slot m of the (b, g) staging row.
+template <int KV, int D, int BLK>
+__device__ __forceinline__ ItemDesc describe_sparse(const AttnParams& p, int b, int g, int m, int j,
+                                                    int64_t phys, int sub) {
+  using C = AttnCfg<KV, D, BLK>;
+  ItemDesc d;
+  d.ks = 1.f;
+  d.vs = 1.f;
+  d.pos0 = j * BLK + sub * C::TB;
+  if (p.sparse_kind == SKV_SRC_PAGED) {
+    if (phys < 0) phys = p.block_table[(int64_t)b * p.max_blocks + j];
+    d.off = phys * p.stride_block + (int64_t)g * p.stride_head;
+    if (KV == KV_FP8) {
+      d.ks = p.sks[phys * p.Hkv + g];
+      d.vs = p.svs[phys * p.Hkv + g];
+    }
+  } else {
+    const int64_t slot = ((int64_t)b * p.Hkv + g) * p.k_max + m;
+    d.off = slot * BLK * D;
+    if (KV == KV_FP8) {
+      d.ks = p.sks[slot];
+      d.vs = p.svs[slot];
+    }
+  }
+  d.off += (int64_t)sub * C::TB * D;
+  return d;
+}
+
+// Slice `sub` of the c-th block of (b, g)'s recent window (window start ws).
+template <int KV, int D, int BLK>
+__device__ __forceinline__ ItemDesc describe_window(const AttnParams& p, int b, int g, int c, int sub, int ws) {
+  using C = AttnCfg<KV, D, BLK>;
+  ItemDesc d;
+  d.ks = 1.f;
+  d.vs = 1.f;
+  if (p.window_kind == SKV_SRC_PAGED) {
+    const int j = ws / BLK + c;
+    d.pos0 = j * BLK + sub * C::TB;
+    const int64_t phys = p.window_table[(int64_t)b * p.max_blocks + j];
+    d.off = phys * p.stride_block + (int64_t)g * p.stride_head;
+    if (KV == KV_FP8) {
+      d.ks = p.wks[phys * p.Hkv + g];
+      d.vs = p.wvs[phys * p.Hkv + g];
+    }
+  } else {
+    d.pos0 = ws + c * BLK + sub * C::TB;
+    d.off = (((int64_t)b * p.Hkv + g) * p.window + (int64_t)c * BLK) * D;
+  }
+  d.pos0 |= (int)0x80000000;
+  d.off += (int64_t)sub * C::TB * D;
+  return d;
+}
+
+// Item `item` of (b, g)'s list: slices of the nsel selected blocks (ids and,
+// when given, physical ids from the selection's output rows), then slices of
+// the window blocks.
+template <int KV, int D, int BLK>
+__device__ __forceinline__ ItemDesc describe(const AttnParams& p, int b, int g, int item, int nsel, int ws) {
+  using C = AttnCfg<KV, D, BLK>;
+  const int blk_item = item / C::SUB, sub = item % C::SUB;
+  if (blk_item < nsel) {
+    const int64_t row = ((int64_t)b * p.T * p.Hkv + g) * p.k_max + blk_item;
+    // physical ids emitted by the selection save the dependent table lookup
+    return describe_sparse<KV, D, BLK>(p, b, g, blk_item, p.indices[row], p.phys ? p.phys[row] : -1, sub);
+  }
+  return describe_window<KV, D, BLK>(p, b, g, blk_item - nsel, sub, ws);
+}
+
+// LDS bytes of an NW-wave attention workgroup (per-wave V tiles / combine rows).
+template <int KV, int D, int BLK>
+constexpr int attn_lds_bytes(int nw) { return nw * AttnCfg<KV, D, BLK>::PER_WAVE; }
+
+// Window blocks of a sequence of length L (window start ws).
+__device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws) {
+  if (ws >= L || p.window <= 0) return 0;
+  if (p.window_kind == SKV_SRC_PAGED) return (L - 1) / p.blk - ws / p.blk + 1;
+  return (L - ws + p.blk - 1) / p.blk;
+}
+
+// One NW-wave workgroup's attention of (b, g) over items [first, first+count)
+// of a list described by desc(item).  Wave w takes items first + w,
+// first + w + NW, ...; lane j of the wave holds the descriptor of the wave's
+// j-th item.  Items for which early(item) holds are described up front; the
+// others only after the hooks: pre() runs once the query loads are issued,
+// then each wave whose first item is early issues that item's loads, then
+// post() runs (both hooks run in every thread).  Leaves each wave's
+// unnormalised O rows, running max and sum in its LDS combine region.
+template <int KV, int D, int BLK, int NW, class DescFn, class EarlyFn, class PreFn, class PostFn>
+__device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, int b, int g, int first,
+                                             int count, DescFn desc, EarlyFn early, PreFn pre,
+                                             PostFn post) {
+  using C = AttnCfg<KV, D, BLK>;
+  const int lane = lane_id(), w = wave_id();
+  const int n = lane & 15;   // C/B column, A row
+  const int kg = lane >> 4;  // row group / k group
+  const int G = p.G;
+  const int L = p.seq_lens[b];
+  const int ws = L - p.window > 0 ? L - p.window : 0;
+
+  // ---- query operand: column n holds head n (and head n-G for the low half)
+  const int ncols = KV == KV_F32 ? G : 2 * G;
+  const int hq = n < G ? n : (n < ncols ? n - G : -1);
+  uint4 qop[KV == KV_F32 ? 1 : C::KS];
+  float qopf[KV == KV_F32 ? C::KS : 1];
+  {
+    const int64_t qrow = (((int64_t)b * p.T) * p.Hq + (int64_t)g * G + (hq < 0 ? 0 : hq)) * D;
+    if constexpr (KV == KV_F32) {
+      // k-step s of group kg is element 16(s/4) + 4kg + s%4 of the row
+      const float* qp = static_cast<const float*>(p.q) + qrow;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) qopf[s] = hq < 0 ? 0.f : qp[16 * (s / 4) + 4 * kg + (s % 4)];
+    } else {
+      // bf16: k-step s of group kg is elements 32s + 8kg .. +7;
+      // fp8: k-step s is elements 64(s/2) + 16kg + 8(s%2) .. +7
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + qrow;
+#pragma unroll
+      for (int s = 0; s < C::KS; ++s) {
+        const int off = KV == KV_BF16 ? 32 * s + 8 * kg : 64 * (s / 2) + 16 * kg + 8 * (s % 2);
+        qop[s] = hq < 0 ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(qp + off);
+      }
+    }
+  }
+
+  const int my_items = count > w ? (count - w + NW - 1) / NW : 0;  // this wave's items
+  const int my_item = first + w + NW * lane;
+
+  // lane j describes this wave's item j
+  ItemDesc mine{0, 0, 1.f, 1.f};
+  if (lane < my_items && early(my_item)) mine = desc(my_item);
+
+  const char* kbase_s = static_cast<const char*>(p.sk);
+  const char* vbase_s = static_cast<const char*>(p.sv);
+  const char* kbase_w = static_cast<const char*>(p.wk);
+  const char* vbase_w = static_cast<const char*>(p.wv);
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4_t o[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  char* vt = smem + w * C::PER_WAVE;
+  uint4 kr[C::NT][C::GRAN];
+  uint4 vr[C::NV];
+  int pos0 = 0;
+  float ksc = 1.f, vsc = 1.f;
+
+  // Issue the loads of item j (descriptor broadcast from lane j).
+  auto load_item = [&](int j) {
+    const int lo32 = __builtin_amdgcn_readlane((int)(uint32_t)mine.off, j);
+    const int hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)mine.off >> 32), j);
+    const int64_t off = (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);
+    pos0 = __builtin_amdgcn_readlane(mine.pos0, j);
+    ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.ks), j));
+    vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.vs), j));
+    const bool win = pos0 < 0;
+    const char* kb = (win ? kbase_w : kbase_s) + off * C::ES;
+    const char* vb = (win ? vbase_w : vbase_s) + off * C::ES;
+#pragma unroll
+    for (int tile = 0; tile < C::NT; ++tile) {
+      const char* krow = kb + (16 * tile + n) * (D * C::ES) + 16 * kg;
+#pragma unroll
+      for (int q = 0; q < C::GRAN; ++q) kr[tile][q] = load_stream16(krow + 64 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < C::NV; ++i) vr[i] = load_stream16(vb + 16 * (lane + kWave * i));
+  };
+
+  pre();
+  const bool first_early = my_items > 0 && early(first + w);
+  if (first_early) load_item(0);
+  post();
+  if (lane < my_items && !early(my_item)) mine = desc(my_item);
+  if (my_items > 0 && !first_early) load_item(0);
+
+  for (int j = 0; j < my_items; ++j) {
+    const bool win = pos0 < 0;
+    const int p0 = pos0 & 0x7fffffff;
+    const int lo = win ? ws : 0;
+    const int hi = win ? L : ws;
+    const float ks_cur = ksc, vs_cur = vsc;
+
+    // ---- S^T = K Q^T
+    f32x4_t st[C::NT];
+#pragma unroll
+    for (int tile = 0; tile < C::NT; ++tile) {
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KV == KV_BF16) {
+#pragma unroll
+        for (int q = 0; q < C::GRAN; ++q) acc = mfma_bf16(kr[tile][q], qop[q], acc);
+      } else if constexpr (KV == KV_FP8) {
+#pragma unroll
+        for (int q = 0; q < C::GRAN; ++q) {
+          uint4 lo16, hi16;
+          fp8x16_to_bf16x16(kr[tile][q], lo16, hi16);
+          acc = mfma_bf16(lo16, qop[2 * q], acc);
+          acc = mfma_bf16(hi16, qop[2 * q + 1], acc);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < C::GRAN; ++q) {
+          acc = mfma_f32(__uint_as_float(kr[tile][q].x), qopf[4 * q + 0], acc);
+          acc = mfma_f32(__uint_as_float(kr[tile][q].y), qopf[4 * q + 1], acc);
+          acc = mfma_f32(__uint_as_float(kr[tile][q].z), qopf[4 * q + 2], acc);
+          acc = mfma_f32(__uint_as_float(kr[tile][q].w), qopf[4 * q + 3], acc);
+        }
+      }
+      st[tile] = acc;
+    }
+
+    // ---- V -> LDS (token-major rows; rows outside [lo, hi) become zero)
+    const bool partial = p0 < lo || p0 + C::TB > hi;
+#pragma unroll
+    for (int i = 0; i < C::NV; ++i) {
+      const int off = 16 * (lane + kWave * i);
+      const int row = off / (D * C::ES);
+      const int col = off % (D * C::ES);
+      const bool ok = !partial || (p0 + row >= lo && p0 + row < hi);
+      if constexpr (KV == KV_FP8) {
+        uint4 a, c;
+        fp8x16_to_bf16x16(vr[i], a, c);
+        if (!ok) a = c = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(vt + row * C::VROW + 2 * col) = a;
+        *reinterpret_cast<uint4*>(vt + row * C::VROW + 2 * col + 16) = c;
+      } else {
+        uint4 val = vr[i];
+        if (partial && !ok) val = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(vt + row * C::VROW + col) = val;
+      }
+    }
+
+    // ---- prefetch the next item while this one finishes
+    if (j + 1 < my_items) load_item(j + 1);
+
+    // ---- online softmax (log2 domain)
+    const float sc = p.qk_scale * ks_cur;
+    float bm = -INFINITY;
+#pragma unroll
+    for (int tile = 0; tile < C::NT; ++tile)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pos = p0 + 16 * tile + 4 * kg + r;
+        float z = st[tile][r] * sc;
+        z = (pos >= lo && pos < hi) ? z : -INFINITY;
+        st[tile][r] = z;
+        bm = fmaxf(bm, z);
+      }
+    bm = fmaxf(bm, shfl_xor_f(bm, 16));
+    bm = fmaxf(bm, shfl_xor_f(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    const bool none = m_new == -INFINITY;
+    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int tile = 0; tile < C::NT; ++tile)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pv = none ? 0.f : exp2f(st[tile][r] - m_new);
+        st[tile][r] = pv;
+        psum += pv;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    if (__ballot(n < ncols && alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * kg + i;
+        const int head = row < ncols ? row % G : 0;
+        const float a = shfl_f(alpha, head);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) o[dt][i] *= a;
+      }
+    }
+
+    wave_lds_sync();
+
+    // ---- O += P V
+    if constexpr (KV == KV_F32) {
+#pragma unroll
+      for (int tile = 0; tile < C::NT; ++tile)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = n < G ? st[tile][r] : 0.f;
+          const char* vrow = vt + (16 * tile + 4 * kg + r) * C::VROW + 4 * n;
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+            o[dt] = mfma_f32(a, *reinterpret_cast<const float*>(vrow + 64 * dt), o[dt]);
+        }
+    } else {
+      // P operand: element e of lane (n, kg) is token 4kg + e%4 of tile e/4
+      uint32_t pw[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        constexpr int NT = C::NT;
+        const int t0 = (2 * e2) / 4;
+        f32x2_t pv = {t0 < NT ? st[t0 < NT ? t0 : 0][(2 * e2) % 4] : 0.f,
+                      t0 < NT ? st[t0 < NT ? t0 : 0][(2 * e2 + 1) % 4] : 0.f};
+        if constexpr (KV == KV_FP8) pv *= vs_cur;
+        const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf16x2_t));
+        const f32x2_t rest = {pv.x - bf16_lo(hw), pv.y - bf16_hi(hw)};
+        const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_t));
+        pw[e2] = n < G ? hw : (n < ncols ? lw : 0u);
+      }
+      const uint4 aop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      // B operand: lane r of row group kg reads row 4kg + r/4 (and +16), columns
+      // 16dt + 4(r%4) .. +3; the transposing read hands lane n column 16dt + n of
+      // those four rows, i.e. tokens 4kg .. 4kg+3 of each tile.
+      const char* tbase = vt + (4 * kg + (n >> 2)) * C::VROW + 8 * (n & 3);
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(tbase + 32 * dt));
+        i16x4_t hi4 = i16x4_t{0, 0, 0, 0};
+        if constexpr (C::NT > 1)
+          hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(tbase + 16 * C::VROW + 32 * dt));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo4);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi4);
+        o[dt] = mfma_bf16(aop, make_uint4(l2.x, l2.y, h2.x, h2.y), o[dt]);
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // ---- combine the waves in LDS
+  float lsum = l_run;
+  lsum += shfl_xor_f(lsum, 16);
+  lsum += shfl_xor_f(lsum, 32);
+  __syncthreads();
+  {
+    float* comb = reinterpret_cast<float*>(smem + w * C::PER_WAVE);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) comb[(4 * kg + i) * D + 16 * dt + n] = o[dt][i];
+    if (kg == 0) {
+      comb[16 * D + n] = m_run;
+      comb[16 * D + 16 + n] = lsum;
+    }
+  }
+  __syncthreads();
+}
+
+// Combine the NW waves' regions into the workgroup's partial for split
+// `split` of n_splits; a single split writes the output directly, otherwise
+// the last split of (b, g) to arrive merges all of them.  `ready`, when given,
+// is the pair's ready flag, cleared once every split of the pair is done.
+template <int KV, int D, int BLK, int NW>
+__device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, int b, int g, int split,
+                                              int n_splits, int* s_last, unsigned* ready) {
+  using C = AttnCfg<KV, D, BLK>;
+  constexpr int NTH = NW * kWave;
+  const int G = p.G;
+  const int64_t pair = (int64_t)b * p.Hkv + g;
+  float* part = p.partials + (pair * n_splits + split) * G * (D + 2);
+  for (int idx = threadIdx.x; idx < G * D; idx += NTH) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww)
+      M = fmaxf(M, reinterpret_cast<const float*>(smem + ww * C::PER_WAVE)[16 * D + h]);
+    float O = 0.f, Ls = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* comb = reinterpret_cast<const float*>(smem + ww * C::PER_WAVE);
+        const float mw = comb[16 * D + h];
+        if (mw == -INFINITY) continue;
+        const float f = exp2f(mw - M);
+        float ov = comb[h * D + d];
+        if constexpr (KV != KV_F32) ov += comb[(G + h) * D + d];
+        O += f * ov;
+        Ls += f * comb[16 * D + 16 + h];
+      }
+    }
+    if (n_splits == 1) {
+      // a single split is the whole attention of (b, g): write the result directly
+      const int64_t bh = (int64_t)b * p.Hq + (int64_t)g * G + h;
+      p.out[bh * D + d] = M == -INFINITY ? 0.f : O / Ls;
+      if (d == 0 && p.lse) p.lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(Ls)) * kLn2;
+      continue;
+    }
+    publish_f32(part + h * (D + 2) + 2 + d, O);
+    if (d == 0) {
+      publish_f32(part + h * (D + 2), M);
+      publish_f32(part + h * (D + 2) + 1, Ls);
+    }
+  }
+  if (n_splits == 1) {
+    if (ready && threadIdx.x == 0) __hip_atomic_store(ready + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+
+  // ---- the last split of (b, g) merges every split
+  if (!arrive_last(p.counters + pair, (unsigned)n_splits, s_last)) return;
+  // every split has passed its wait on the pair's ready flag: clear it for the next launch
+  if (ready && threadIdx.x == 0) __hip_atomic_store(ready + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float* pb = p.partials + pair * n_splits * G * (D + 2);
+  // per (split, head): maxima and sums, then normalised weights 2^(m - M) / L
+  float* mm = reinterpret_cast<float*>(smem);   // [n_splits][G]
+  float* ll = mm + n_splits * G;                 // [n_splits][G]
+  float* wgt = ll + n_splits * G;                // [n_splits][G]
+  float* hres = wgt + n_splits * G;              // [G] lse in log2 units
+  for (int i = threadIdx.x; i < n_splits * G; i += NTH) {
+    const int s = i / G, h = i % G;
+    mm[i] = fetch_f32(pb + ((int64_t)s * G + h) * (D + 2));
+    ll[i] = fetch_f32(pb + ((int64_t)s * G + h) * (D + 2) + 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, mm[s * G + h]);
+    float Ls = 0.f;
+    if (M != -INFINITY)
+      for (int s = 0; s < n_splits; ++s)
+        if (mm[s * G + h] != -INFINITY) Ls += exp2f(mm[s * G + h] - M) * ll[s * G + h];
+    for (int s = 0; s < n_splits; ++s)
+      wgt[s * G + h] = (M == -INFINITY || mm[s * G + h] == -INFINITY) ? 0.f
+                                                                     : exp2f(mm[s * G + h] - M) / Ls;
+    hres[h] = M == -INFINITY ? -INFINITY : M + log2f(Ls);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += NTH) {
+    const int h = idx / D, d = idx % D;
+    float acc = 0.f;
+    constexpr int SB = 8;
+    for (int s0 = 0; s0 < n_splits; s0 += SB) {
+      float v[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        v[u] = (s0 + u < n_splits) ? fetch_f32(pb + ((int64_t)(s0 + u) * G + h) * (D + 2) + 2 + d) : 0.f;
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+        if (s0 + u < n_splits) acc += wgt[(s0 + u) * G + h] * v[u];
+    }
+    const int64_t bh = (int64_t)b * p.Hq + (int64_t)g * G + h;
+    p.out[bh * D + d] = acc;
+    if (d == 0 && p.lse) p.lse[bh] = hres[h] == -INFINITY ? -INFINITY : hres[h] * kLn2;
+  }
+}
+
+}  // namespace skv

@@ -1,0 +1,461 @@
+// select_dev.h -- device code of landmark scoring and per-KV-head top-k
+// block selection, shared by the stand-alone kernels and the single-launch
+// decode step.
+//
+// Scoring (DualDecoder review, core claim and axiom ledger item 1: the
+// retrieval index follows from the query and the landmarks resident on the
+// GPU): score(b,t,g,j) = qbar(b,t,g) . landmark(b,g,j), where qbar is the sum
+// of the G query heads of KV head g.  Summing the heads first turns the
+// group's G dot products into one, so scoring is a streaming gemv over the
+// landmarks: each landmark row is read once with 16-byte loads (16 lanes per
+// 256-byte bf16 row) and serves both query tokens of a dual-query step.
+//
+// Selection (PulseInfer article, section 2: per-head sparse selection;
+// DualDecoder ledger: a budget of k blocks): an LDS radix select on
+// order-preserving 32-bit keys (four 8-bit passes) finds the k-th largest key;
+// blocks above it are kept, blocks equal to it are kept in ascending id order
+// until k are chosen (ties to the lowest id), and the chosen ids are written
+// in ascending order after one block-wide scan.
+//
+// NT is the workgroup size.  PUB selects device-scope atomic stores for the
+// selection results, for readers in other workgroups of the same launch.
+// Workgroup barriers here hand off LDS only (lds_barrier), so global loads a
+// caller issued before a selection stay in flight through it.
+#pragma once
+
+#include "skv_device.h"
+#include "skv_internal.h"
+
+namespace skv {
+
+// Inclusive prefix sum across the 64 lanes of a wave with DPP row shifts and
+// row broadcasts (no LDS round trips).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix sum over the NT threads of a workgroup (one barrier; the
+// caller alternates `lds_w` between two buffers on consecutive calls).
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds_w, uint32_t& total) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id(), w = wave_id();
+  const uint32_t x = wave_inclusive_scan(v);
+  if (lane == kWave - 1) lds_w[w] = x;
+  lds_barrier();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t t = lds_w[i];
+    base += (i < w) ? t : 0u;
+    tot += t;
+  }
+  total = tot;
+  return base + x - v;
+}
+
+template <int NT>
+struct TopkShared {
+  uint32_t hist[2][256];
+  uint32_t scan_w[2][NT / kWave];
+  uint32_t digit, above, common;
+};
+
+template <bool PUB>
+__device__ __forceinline__ void put_i32(int32_t* p, int32_t v) {
+  if constexpr (PUB) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool PUB>
+__device__ __forceinline__ void put_f32(float* p, float v) {
+  if constexpr (PUB) publish_f32(p, v);
+  else *p = v;
+}
+
+// Select the k largest of keys[0..n) (ties to the lowest index).  Writes the
+// chosen indices in ascending order to out[0..k') and -1 to out[k'..k_max);
+// mirrors them to lds_out.  Returns k' = clamp(min(k, n), 0, k_max).
+//
+// Radix select on 8-bit digits, most significant first: each pass builds the
+// histogram of the digit among the keys that match the known prefix, one wave
+// finds the digit holding the k'-th largest key, and after four passes that
+// key T is known exactly.  Keys above T are all kept; keys equal to T are kept
+// in ascending index order until k' are chosen.
+template <int NT, bool PUB>
+__device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32_t* out,
+                                            int32_t* lds_out, TopkShared<NT>& sh) {
+  static_assert(NT >= 256, "the histogram is cleared by the first 256 threads");
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  int kk = k < n ? k : n;
+  if (kk > k_max) kk = k_max;  // the output row holds k_max entries
+  if (kk < 0) kk = 0;
+  const bool take_all = kk >= n;
+  uint32_t thresh = 0, take_eq = 0;
+  if (!take_all && kk > 0) {
+    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kk;
+    if (tid < 256) sh.hist[0][tid] = 0;
+    lds_barrier();
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      uint32_t* hist = sh.hist[pass & 1];
+      for (int j = tid; j < n; j += NT) {
+        const uint32_t key = keys[j];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      lds_barrier();
+      if (w == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending)
+        uint32_t c[4], lsum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[i] = hist[255 - 4 * lane - i];
+          lsum += c[i];
+        }
+        uint32_t above = wave_inclusive_scan(lsum) - lsum;  // keys in higher digits
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (above < remaining && above + c[i] >= remaining) {
+            sh.digit = 255u - 4 * lane - i;
+            sh.above = above;
+          }
+          above += c[i];
+        }
+      } else if (w == 1) {
+        // meanwhile wave 1 clears the other histogram for the next pass
+        for (int t = lane; t < 256; t += kWave) sh.hist[(pass + 1) & 1][t] = 0;
+      }
+      lds_barrier();
+      prefix |= sh.digit << shift;
+      pmask |= 255u << shift;
+      remaining -= sh.above;
+    }
+    thresh = prefix;
+    take_eq = remaining;
+  }
+  // Emit in ascending index order: thread tid owns indices [j0, j1).
+  const int per = (n + NT - 1) / NT;
+  const int j0 = tid * per;
+  const int j1 = min(n, j0 + per);
+  uint32_t gt = 0, eq = 0;
+  if (!take_all && kk > 0)
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = keys[j];
+      gt += key > thresh;
+      eq += key == thresh;
+    }
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan<NT>((gt << 16) | eq, sh.scan_w[0], tot);
+  if (take_all) {
+    for (int j = j0; j < j1; ++j) {
+      put_i32<PUB>(out + j, j);
+      lds_out[j] = j;
+    }
+  } else if (kk > 0) {
+    const uint32_t gt_before = ex >> 16, eq_before = ex & 0xffffu;
+    int pos = (int)(gt_before + min(eq_before, take_eq));
+    uint32_t eq_seen = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = keys[j];
+      bool keep = key > thresh;
+      if (key == thresh) {
+        keep = eq_seen < take_eq;
+        ++eq_seen;
+      }
+      if (keep) {
+        put_i32<PUB>(out + pos, j);
+        lds_out[pos] = j;
+        ++pos;
+      }
+    }
+  }
+  const int nsel = take_all ? n : kk;
+  for (int m = nsel + tid; m < k_max; m += NT) {
+    put_i32<PUB>(out + m, -1);
+    lds_out[m] = -1;
+  }
+  lds_barrier();  // scan buffer and lds_out are reused by the caller
+  return nsel;
+}
+
+// |a & b| / |a| for two ascending index lists in LDS (1 when a is empty).
+template <int NT>
+__device__ __forceinline__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb,
+                                              TopkShared<NT>& sh) {
+  if (threadIdx.x == 0) sh.common = 0;
+  lds_barrier();
+  uint32_t local = 0;
+  for (int i = threadIdx.x; i < na; i += NT) {
+    const int x = a[i];
+    int lo = 0, hi = nb;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (b[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    local += (lo < nb && b[lo] == x) ? 1u : 0u;
+  }
+  if (local) atomicAdd(&sh.common, local);
+  lds_barrier();
+  return na > 0 ? (float)sh.common / (float)na : 1.0f;
+}
+
+__device__ __forceinline__ int n_candidates(int L, int window, int blk) {
+  const int ws = L - window > 0 ? L - window : 0;
+  return (ws + blk - 1) / blk;
+}
+
+// Keys of one token's row from a score array in global memory into LDS.
+template <int NT>
+__device__ __forceinline__ void load_keys(const float* row, int nc, bool coherent, uint32_t* keys) {
+  constexpr int KB = 8;  // loads in flight per thread
+  for (int j0 = threadIdx.x; j0 < nc; j0 += KB * NT) {
+    float v[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = j0 + u * NT;
+      v[u] = j < nc ? (coherent ? fetch_f32(row + j) : row[j]) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int j = j0 + u * NT;
+      if (j < nc) keys[j] = score_key(v[u]);
+    }
+  }
+}
+
+// Selection for one (b, g) and every query token.  Token t's keys are at
+// keys + t * key_stride (already there when `scores` is null, else loaded
+// from scores + t * t_stride).
+template <int NT, bool PUB>
+__device__ __forceinline__ void select_rows(const float* scores, int64_t t_stride, bool coherent,
+                                            uint32_t* keys, int key_stride, int nc, int T, int k,
+                                            int k_max, int32_t* indices, int64_t idx_t_stride,
+                                            int32_t* n_sel, int64_t nsel_t_stride, float* overlap_out,
+                                            int32_t* lds_idx, TopkShared<NT>& sh) {
+  int ns0 = 0, ns1 = 0;
+  for (int t = 0; t < T; ++t) {
+    uint32_t* kt = keys + t * key_stride;
+    if (scores) {
+      load_keys<NT>(scores + t * t_stride, nc, coherent, kt);
+      lds_barrier();
+    }
+    const int ns = block_select<NT, PUB>(kt, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
+    if (t == 0) ns0 = ns; else ns1 = ns;
+    if (threadIdx.x == 0) put_i32<PUB>(n_sel + t * nsel_t_stride, ns);
+    lds_barrier();
+  }
+  if (T == 2 && overlap_out) {
+    const float ov = list_overlap<NT>(lds_idx, ns0, lds_idx + k_max, ns1, sh);
+    if (threadIdx.x == 0) put_f32<PUB>(overlap_out, ov);
+  }
+}
+
+// Physical block of every selected index (row b of the block table).
+template <int NT, bool PUB>
+__device__ __forceinline__ void write_phys(const int32_t* lds_idx, int T, int k_max,
+                                           const int32_t* table_row, int32_t* phys,
+                                           int64_t t_stride) {
+  lds_barrier();
+  for (int i = threadIdx.x; i < T * k_max; i += NT) {
+    const int t = i / k_max, m = i % k_max;
+    const int j = lds_idx[i];
+    put_i32<PUB>(phys + t * t_stride + m, j >= 0 ? table_row[j] : -1);
+  }
+}
+
+// Landmark scoring of (b, g) rows of chunk c.  Modes: stand-alone scoring
+// (scores to global, -inf past the candidates); fused with one chunk per
+// (b, g) (scores go straight to the LDS keys for the selection); fused with
+// several chunks (scores are published to the workspace for the chunk that
+// selects).  Returns false when a fused chunk has no rows.  `smem` holds
+// score_lds_bytes().
+template <int D, bool LM_F32, bool Q_F32, int NT, int UR>
+__device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, int b, uint32_t* smem) {
+  constexpr int NW = NT / kWave;
+  constexpr int ES = LM_F32 ? 4 : 2;
+  constexpr int LPR = D * ES / 16;      // lanes per landmark row
+  constexpr int EPL = 16 / ES;          // landmark elements per lane
+  constexpr int RPW = kWave / LPR;      // rows per wave per step
+  constexpr int RPS = RPW * NW;         // rows per workgroup per step
+  static_assert(2 * D <= NT, "the group-summed query needs T * D threads");
+
+  const int T = p.T;
+  const int L = p.seq_lens[b];
+  const int nc = n_candidates(L, p.window, p.blk);
+  const int R = p.rows_per_chunk;
+  int row_begin, row_end, nchunks = 1;
+  if (p.fused_select) {
+    nchunks = max(1, (nc + R - 1) / R);
+    if (c >= nchunks) return false;
+    row_begin = c * R;
+    row_end = min(nc, row_begin + R);
+  } else {
+    row_begin = c * R;
+    row_end = min(p.max_blocks, row_begin + R);
+  }
+  const bool in_lds = p.fused_select && p.single_chunk;
+
+  float* qbar = reinterpret_cast<float*>(smem);  // [T][D]
+  uint32_t* keys = smem + T * D;                 // [T][score_cols]
+
+  const int lane = lane_id(), w = wave_id();
+  const int sub = lane % LPR, rw = lane / LPR;
+  const char* lm = static_cast<const char*>(p.landmarks) +
+                   ((int64_t)(b * p.Hkv + g) * p.max_blocks) * D * ES + sub * 16;
+  const int steps = (row_end - row_begin + RPS - 1) / RPS;
+
+  // Rows past the range are loaded from the last valid row (and ignored), so
+  // the loads carry no branches and all of a batch is in flight together.
+  const int last_row = max(row_begin, min(row_end, nc) - 1);
+  // Two batches alternate (software pipelining): the next batch's loads are
+  // issued before the current one is consumed, so each wave streams while it
+  // computes.
+  uint4 va[UR], vb[UR];
+  auto load_batch = [&](uint4 (&v)[UR], int s0) {
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int r = min(row_begin + (s0 + u) * RPS + w * RPW + rw, last_row);
+      v[u] = load_stream16(lm + (int64_t)r * D * ES);
+    }
+  };
+  const bool any_rows = row_end > row_begin && nc > 0;
+
+  // group-summed query: its G loads per element are issued first (they are
+  // few), then the first landmark batch, so waiting for the query leaves the
+  // landmark loads in flight
+  const int qi = threadIdx.x;
+  const bool q_owner = qi < T * D;
+  uint32_t qraw[8];
+  {
+    const int t = q_owner ? qi / D : 0, d = q_owner ? qi % D : 0;
+    const int64_t base = ((int64_t)(b * T + t) * p.Hq + (int64_t)g * p.G) * D + d;
+    if constexpr (Q_F32) {
+      const uint32_t* qp = static_cast<const uint32_t*>(p.q) + base;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) qraw[h] = qp[(int64_t)min(h, p.G - 1) * D];
+    } else {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + base;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) qraw[h] = qp[(int64_t)min(h, p.G - 1) * D];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // q loads issue first: waiting on them leaves the batch in flight
+  load_batch(va, 0);   // always in bounds (clamped rows); results are ignored without rows
+  if (q_owner) {
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 8; ++h)
+      sum += h < p.G ? (Q_F32 ? __uint_as_float(qraw[h]) : __uint_as_float(qraw[h] << 16)) : 0.f;
+    qbar[qi] = sum;
+  }
+  lds_barrier();
+  float qr[2][EPL];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qr[t][e] = (t < T) ? qbar[t * D + sub * EPL + e] : 0.f;
+
+  float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
+  const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
+
+  auto consume = [&](const uint4 (&v)[UR], int s0) {
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+      const int r = row_begin + (s0 + u) * RPS + w * RPW + rw;
+      float x[EPL];
+      if constexpr (LM_F32) {
+        x[0] = __uint_as_float(v[u].x); x[1] = __uint_as_float(v[u].y);
+        x[2] = __uint_as_float(v[u].z); x[3] = __uint_as_float(v[u].w);
+      } else {
+        x[0] = bf16_lo(v[u].x); x[1] = bf16_hi(v[u].x); x[2] = bf16_lo(v[u].y); x[3] = bf16_hi(v[u].y);
+        x[4] = bf16_lo(v[u].z); x[5] = bf16_hi(v[u].z); x[6] = bf16_lo(v[u].w); x[7] = bf16_hi(v[u].w);
+      }
+      float acc[2] = {0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[0] = fmaf(qr[0][e], x[e], acc[0]);
+      acc[0] = group_sum<LPR>(acc[0]);
+      if (T == 2) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[1] = fmaf(qr[1][e], x[e], acc[1]);
+        acc[1] = group_sum<LPR>(acc[1]);
+      }
+      if (sub == 0 && s0 + u < steps && r < row_end) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          if (t >= T) break;
+          float val = acc[t];
+          if (val == 0.0f) val = 0.0f;  // one zero
+          if (in_lds) {
+            keys[t * p.score_cols + r] = score_key(val);
+          } else {
+            val = (r < nc) ? val : -INFINITY;
+            if (p.fused_select) publish_f32(sc + t * t_stride + r, val);
+            else sc[t * t_stride + r] = val;
+          }
+        }
+      }
+    }
+  };
+  // The loads are unconditional (rows past the range re-read the last row,
+  // and consume() stores nothing for them): a conditional batch would make
+  // the wait before each consume() count the next batch's loads as well.
+  for (int s0 = 0; s0 < steps && any_rows; s0 += 2 * UR) {
+    load_batch(vb, s0 + UR);
+    consume(va, s0);
+    load_batch(va, s0 + 2 * UR);
+    consume(vb, s0 + UR);
+  }
+
+  return true;
+}
+
+// The selection of a fused scoring launch, after score_rows of chunk c:
+// single chunk -- the keys are in LDS; several chunks -- the last chunk of
+// (b, g) to arrive reads the published scores.  Returns true in the
+// workgroup that selected.
+template <int NT, bool PUB>
+__device__ __forceinline__ bool select_scored(const ScoreParams& p, int g, int b, uint32_t* smem,
+                                              TopkShared<NT>& sh, int* s_flag) {
+  const int T = p.T;
+  const int nc = n_candidates(p.seq_lens[b], p.window, p.blk);
+  const int nchunks = max(1, (nc + p.rows_per_chunk - 1) / p.rows_per_chunk);
+  uint32_t* keys = smem + T * p.D;
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + T * p.score_cols);
+  float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
+  const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
+  const int k = p.k_per_seq[b];
+  int32_t* idx_out = p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max;
+  int32_t* nsel_out = p.n_sel + (int64_t)b * T * p.Hkv + g;
+  float* ov_out = p.overlap ? p.overlap + b * p.Hkv + g : nullptr;
+  if (p.single_chunk) {
+    lds_barrier();
+    select_rows<NT, PUB>(nullptr, 0, false, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
+                         (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
+  } else {
+    // ---- several chunks: the last one of (b, g) to arrive selects
+    if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, s_flag)) return false;
+    select_rows<NT, PUB>(sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
+                         (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
+  }
+  if (p.phys)
+    write_phys<NT, PUB>(lds_idx, T, p.k_max, p.block_table + (int64_t)b * p.max_blocks,
+                        p.phys + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max);
+  return true;
+}
+
+// Scoring of chunk c of (b, g), then (fused) the selection; see score_rows
+// and select_scored.
+template <int D, bool LM_F32, bool Q_F32, int NT, int UR, bool PUB>
+__device__ __forceinline__ bool score_task(const ScoreParams& p, int c, int g, int b, uint32_t* smem,
+                                           TopkShared<NT>& sh, int* s_flag) {
+  if (!score_rows<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, smem)) return false;
+  if (!p.fused_select) return false;
+  return select_scored<NT, PUB>(p, g, b, smem, sh, s_flag);
+}
+
+}  // namespace skv

@@ -152,6 +152,9 @@ __device__ __forceinline__ void publish_f32(float* p, float v) {
 __device__ __forceinline__ float fetch_f32(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int32_t fetch_i32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void wait_own_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Called by every thread after its publish_f32 stores; returns true in the

@@ -102,6 +102,11 @@ struct Plan {
   int max_cand;             // upper bound of candidates per sequence
   int rows_per_chunk, score_chunks;
   int items_per_split, n_splits;   // attention split-K
+  // single-launch step: one workgroup per (sequence, KV head) scores,
+  // selects and attends (fused_step = 1 when the shape has that kernel and
+  // there are enough pairs to fill the chip)
+  int fused_step;
+  size_t step_lds;          // dynamic LDS bytes of the step kernel (scoring region)
   size_t off_score_counters, off_attn_counters, off_scores, off_partials, off_phys, total_bytes;
 };
 
@@ -110,8 +115,20 @@ Plan make_plan(const skv_problem& pr);
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(const AttnParams& p, hipStream_t s);
+hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hipStream_t st);
+// Whether a step kernel is built for this shape (device pool, d = 128, bf16
+// queries and landmarks, bf16 or fp8 K/V, blocks of 32 or 64 tokens).
+bool step_kernel_available(const skv_problem& p);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
+
+// LDS bytes of a scoring workgroup: qbar [T][d] floats, keys [T][score_cols]
+// (fused selection only) and the selected ids [2][k_max].
+__host__ __device__ inline size_t score_lds_bytes(int T, int D, int score_cols, int k_max, bool fused) {
+  size_t b = (size_t)T * D * 4;
+  if (fused) b += (size_t)T * score_cols * 4 + (size_t)2 * k_max * 4;
+  return b;
+}
 
 // LDS bytes the score kernel needs for a fused selection over max_cand keys.
 size_t topk_lds_bytes(int max_cand);

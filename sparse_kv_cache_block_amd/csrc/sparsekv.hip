@@ -2,6 +2,7 @@
 // validation, launch planning, workspace carving, stream/event ordering.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -90,6 +91,12 @@ constexpr int kScoreSinglePairs = 128;       // from this many pairs on, one sco
 constexpr int kScoreTargetWorkgroups = 256;
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// single-launch step: used from this many (sequence, KV head) pairs on (one
+// 8-wave workgroup per pair and compute unit), with at most this much LDS for
+// the scoring region
+constexpr int kStepMinPairs = 128;
+constexpr size_t kStepMaxScoreLds = 48 * 1024;
+
 }  // namespace
 
 Plan make_plan(const skv_problem& p) {
@@ -122,6 +129,15 @@ Plan make_plan(const skv_problem& p) {
   pl.items_per_split = ips;
   pl.n_splits = (total_items + ips - 1) / ips;
   const int total = pl.n_splits;
+
+  // single-launch step
+  pl.fused_step = 0;
+#ifndef SKV_NO_STEP_KERNEL
+  if (step_kernel_available(p) && pairs >= kStepMinPairs) {
+    pl.step_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true);
+    pl.fused_step = pl.step_lds <= kStepMaxScoreLds;
+  }
+#endif
   size_t off = 0;
   pl.off_score_counters = off;
   off = align256(off + (size_t)pairs * 4);
@@ -283,6 +299,34 @@ skv_status enqueue_attend_paged(const skv_problem& p, const Plan& pl, const skv_
   a.n_sel = out.n_sel;
   a.phys = reinterpret_cast<const int32_t*>(ws + pl.off_phys);
   SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  return SKV_OK;
+}
+
+// The whole device-pool step as one launch (step.hip).
+skv_status enqueue_step(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                        const skv_step_outputs& out, char* ws, hipStream_t s) {
+  ScoreParams sp = score_params(p, in.q, in.landmarks, in.seq_lens);
+  sp.scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  sp.score_cols = pl.max_cand > 0 ? pl.max_cand : 1;
+  sp.rows_per_chunk = sp.score_cols;   // one chunk: the scores stay in LDS
+  sp.fused_select = 1;
+  sp.single_chunk = 1;
+  sp.k_per_seq = in.k_per_seq;
+  sp.indices = out.indices;
+  sp.n_sel = out.n_sel;
+  sp.overlap = p.n_q_tokens == 2 ? out.overlap : nullptr;
+  sp.counters = reinterpret_cast<unsigned*>(ws + pl.off_score_counters);
+  AttnParams a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
+  skv_kv_source sparse{SKV_SRC_PAGED, in.k_pool, in.v_pool, in.k_scales, in.v_scales, in.block_table};
+  skv_kv_source win = in.window_k
+      ? skv_kv_source{SKV_SRC_WINDOW, in.window_k, in.window_v, nullptr, nullptr, nullptr}
+      : sparse;
+  SKV_TRY(set_source(p, a, &sparse, true));
+  SKV_TRY(set_source(p, a, &win, false));
+  a.indices = out.indices;
+  a.n_sel = out.n_sel;
+  a.n_splits = 1;
+  SKV_TRY_HIP(launch_step(sp, a, pl.step_lds, s), "decode step launch");
   return SKV_OK;
 }
 
@@ -501,6 +545,7 @@ skv_status sparsekv_decode_step(const skv_problem* pr, const skv_step_inputs* in
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);
   if (p.pool_location == SKV_POOL_DEVICE) {
+    if (pl.fused_step) return enqueue_step(p, pl, *in, *out, ws, s);
     SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
     return enqueue_attend_paged(p, pl, *in, *out, ws, s);
   }

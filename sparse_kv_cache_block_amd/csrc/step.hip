@@ -1,0 +1,82 @@
+// step.hip -- the whole decode step of one (sequence, KV head) in one
+// workgroup, for gfx950: landmark scoring into LDS, the per-head top-k, and
+// the attention over the recent window and the selected blocks, fused by
+// log-sum-exp, in a single launch with one 8-wave workgroup per pair.
+//
+// The window part does not depend on the selection (Beyond abstract: the
+// recent window is attended densely, the older entries sparsely per head), so
+// the workgroup's item list puts the window slices first and each wave issues
+// the loads of its first window slice before the selection starts: the radix
+// select runs in LDS while those loads are in flight, and its barriers wait
+// for LDS traffic only.  The window descriptors and the attention's query
+// operand are loaded before the scoring; the sparse descriptors (block ids from
+// the selection in LDS, physical ids from the block table) after it, while the
+// waves work through their window slices.
+//
+// The arithmetic of every phase is that of the stand-alone kernels
+// (select_dev.h, attend_dev.h).  One workgroup owns a pair, so there is a
+// single split and the output is written without a merge.
+#include "attend_dev.h"
+#include "select_dev.h"
+
+namespace skv {
+
+constexpr int kPairWaves = 8;
+constexpr int kPairThreads = kPairWaves * kWave;
+#ifndef SKV_PAIR_SCORE_UR
+#define SKV_PAIR_SCORE_UR 8
+#endif
+
+template <int KV, int BLK>
+__global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, AttnParams a) {
+  constexpr int D = 128;
+  using C = AttnCfg<KV, D, BLK>;
+  __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<KV, D, BLK>(kPairWaves)];
+  extern __shared__ __attribute__((aligned(16))) uint32_t score_smem[];
+  __shared__ TopkShared<kPairThreads> sh;
+  __shared__ int s_flag;
+
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int L = a.seq_lens[b];
+  const int ws = L - a.window > 0 ? L - a.window : 0;
+  const int nc = n_candidates(L, a.window, a.blk);
+  // the selection returns clamp(min(k, candidates), 0, k_max) blocks
+  int nsel = min(s.k_per_seq[b], nc);
+  nsel = max(0, min(nsel, a.k_max));
+  const int nwin_items = window_blocks(a, L, ws) * C::SUB;
+  const int count = nwin_items + nsel * C::SUB;
+  const int32_t* lds_idx = reinterpret_cast<const int32_t*>(score_smem + s.T * D + s.T * s.score_cols);
+
+  attend_items<KV, D, BLK, kPairWaves>(
+      a, smem, b, g, 0, count,
+      [&](int item) {
+        if (item < nwin_items) return describe_window<KV, D, BLK>(a, b, g, item / C::SUB, item % C::SUB, ws);
+        const int m = (item - nwin_items) / C::SUB;
+        return describe_sparse<KV, D, BLK>(a, b, g, m, lds_idx[m], -1, (item - nwin_items) % C::SUB);
+      },
+      [&](int item) { return item < nwin_items; },
+      [&] { (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR>(s, 0, g, b, score_smem); },
+      [&] { (void)select_scored<kPairThreads, false>(s, g, b, score_smem, sh, &s_flag); });
+  attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag, nullptr);
+}
+
+bool step_kernel_available(const skv_problem& p) {
+  return p.pool_location == SKV_POOL_DEVICE && p.head_dim == 128 && p.q_dtype == SKV_BF16 &&
+         p.landmark_dtype == SKV_BF16 && (p.kv_dtype == SKV_BF16 || p.kv_dtype == SKV_FP8_E4M3FN) &&
+         (p.block_size == 32 || p.block_size == 64);
+}
+
+hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hipStream_t st) {
+  const dim3 grid(a.Hkv, a.B);
+  const dim3 block(kPairThreads);
+  if (a.kv == KV_FP8) {
+    if (a.blk == 32) hipLaunchKernelGGL((pair_step_kernel<KV_FP8, 32>), grid, block, lds, st, s, a);
+    else hipLaunchKernelGGL((pair_step_kernel<KV_FP8, 64>), grid, block, lds, st, s, a);
+  } else {
+    if (a.blk == 32) hipLaunchKernelGGL((pair_step_kernel<KV_BF16, 32>), grid, block, lds, st, s, a);
+    else hipLaunchKernelGGL((pair_step_kernel<KV_BF16, 64>), grid, block, lds, st, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -216,7 +216,9 @@ def test_gather_and_attend_entry_points():
                 if kss is not None:
                     assert np.array_equal(_np(kss)[b, g, :n], okss[b, g, :n])
                     assert np.array_equal(_np(vss)[b, g, :n], ovss[b, g, :n])
-        # attention from the staged copy equals attention straight from the pool
+        # attention from the staged copy equals attention straight from the pool;
+        # the decode step runs as one launch with its own split layout, so the
+        # two agree up to the order of fp32 sums
         out2 = torch.empty_like(st.out)
         lse2 = torch.empty_like(st.lse)
         sparse = B.kv_source(B.SKV_SRC_STAGED, ks, vs, kss, vss)
@@ -224,7 +226,8 @@ def test_gather_and_attend_entry_points():
                              dev.block_table)
         B.sparsekv_attend(pr, dev.q, sparse, st.indices, st.n_sel, window, dev.seq_lens, out2, lse2, st.ws)
         torch.cuda.synchronize()
-        assert torch.equal(out2, st.out) and torch.equal(lse2, st.lse)
+        assert (out2 - st.out).abs().max().item() <= 2e-5
+        assert (lse2 - st.lse).abs().max().item() <= 2e-5
 
 
 def test_host_layer_pipeline_matches_single_steps():
@@ -247,6 +250,28 @@ def test_repeated_calls_reuse_workspace():
         st.run()
     torch.cuda.synchronize()
     assert torch.equal(first, st.out)
+
+
+def test_alternating_inputs_share_one_workspace():
+    # the single-launch step leaves its ticket counter, ready flags and merge
+    # counters at zero; a stale flag would let a later call read the previous
+    # call's selection, so two input sets alternate on one workspace
+    for wl in (configs.LLAMA32K.scaled(batch=2, context=4096),
+               configs.DUAL.scaled(batch=2, context=8192, top_k=30)):
+        announce(f"alternating inputs on one workspace ({wl.name})")
+        steps = [DecodeStep(to_device_for(make_inputs(wl, device="cpu", instance=i))) for i in range(2)]
+        fresh = []
+        for st in steps:
+            st.run()
+            torch.cuda.synchronize()
+            fresh.append((st.indices.clone(), st.out.clone(), st.lse.clone()))
+        steps[1].ws = steps[0].ws
+        for _ in range(3):
+            for st, (idx, out, lse) in zip(steps, fresh):
+                st.run()
+                torch.cuda.synchronize()
+                assert torch.equal(st.indices, idx)
+                assert torch.equal(st.out, out) and torch.equal(st.lse, lse)
 
 
 # ------------------------------------------------------------ full-size workloads
