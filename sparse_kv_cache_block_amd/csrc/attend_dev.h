@@ -194,9 +194,11 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   const int my_items = count > w ? (count - w + NW - 1) / NW : 0;  // this wave's items
   const int my_item = first + w + NW * lane;
 
-  // lane j describes this wave's item j
-  ItemDesc mine{0, 0, 1.f, 1.f};
-  if (lane < my_items && early(my_item)) mine = desc(my_item);
+  // lane j describes this wave's item j; early and late descriptors stay in
+  // separate registers, so reading an early item never waits for the loads
+  // behind a late one
+  ItemDesc d_early{0, 0, 1.f, 1.f}, d_late{0, 0, 1.f, 1.f};
+  if (lane < my_items && early(my_item)) d_early = desc(my_item);
 
   const char* kbase_s = static_cast<const char*>(p.sk);
   const char* vbase_s = static_cast<const char*>(p.sv);
@@ -215,13 +217,18 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   float ksc = 1.f, vsc = 1.f;
 
   // Issue the loads of item j (descriptor broadcast from lane j).
+  auto read_desc = [&](const ItemDesc& d, int j, int64_t& off) {
+    const int lo32 = __builtin_amdgcn_readlane((int)(uint32_t)d.off, j);
+    const int hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)d.off >> 32), j);
+    off = (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);
+    pos0 = __builtin_amdgcn_readlane(d.pos0, j);
+    ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d.ks), j));
+    vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d.vs), j));
+  };
   auto load_item = [&](int j) {
-    const int lo32 = __builtin_amdgcn_readlane((int)(uint32_t)mine.off, j);
-    const int hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)mine.off >> 32), j);
-    const int64_t off = (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);
-    pos0 = __builtin_amdgcn_readlane(mine.pos0, j);
-    ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.ks), j));
-    vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.vs), j));
+    int64_t off;
+    if (early(first + w + NW * j)) read_desc(d_early, j, off);   // uniform branch
+    else read_desc(d_late, j, off);
     const bool win = pos0 < 0;
     const char* kb = (win ? kbase_w : kbase_s) + off * C::ES;
     const char* vb = (win ? vbase_w : vbase_s) + off * C::ES;
@@ -239,7 +246,7 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   const bool first_early = my_items > 0 && early(first + w);
   if (first_early) load_item(0);
   post();
-  if (lane < my_items && !early(my_item)) mine = desc(my_item);
+  if (lane < my_items && !early(my_item)) d_late = desc(my_item);
   if (my_items > 0 && !first_early) load_item(0);
 
   for (int j = 0; j < my_items; ++j) {

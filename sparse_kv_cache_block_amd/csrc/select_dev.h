@@ -274,7 +274,8 @@ __device__ __forceinline__ void write_phys(const int32_t* lds_idx, int T, int k_
 // several chunks (scores are published to the workspace for the chunk that
 // selects).  Returns false when a fused chunk has no rows.  `smem` holds
 // score_lds_bytes().
-template <int D, bool LM_F32, bool Q_F32, int NT, int UR>
+// LDS_KEYS: compiled for the fused single-chunk mode only.
+template <int D, bool LM_F32, bool Q_F32, int NT, int UR, bool LDS_KEYS = false>
 __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, int b, uint32_t* smem) {
   constexpr int NW = NT / kWave;
   constexpr int ES = LM_F32 ? 4 : 2;
@@ -289,7 +290,7 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
   const int nc = n_candidates(L, p.window, p.blk);
   const int R = p.rows_per_chunk;
   int row_begin, row_end, nchunks = 1;
-  if (p.fused_select) {
+  if (LDS_KEYS || p.fused_select) {
     nchunks = max(1, (nc + R - 1) / R);
     if (c >= nchunks) return false;
     row_begin = c * R;
@@ -298,7 +299,7 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
     row_begin = c * R;
     row_end = min(p.max_blocks, row_begin + R);
   }
-  const bool in_lds = p.fused_select && p.single_chunk;
+  const bool in_lds = LDS_KEYS || (p.fused_select && p.single_chunk);
 
   float* qbar = reinterpret_cast<float*>(smem);  // [T][D]
   uint32_t* keys = smem + T * D;                 // [T][score_cols]
@@ -401,14 +402,25 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
       }
     }
   };
-  // The loads are unconditional (rows past the range re-read the last row,
-  // and consume() stores nothing for them): a conditional batch would make
-  // the wait before each consume() count the next batch's loads as well.
-  for (int s0 = 0; s0 < steps && any_rows; s0 += 2 * UR) {
-    load_batch(vb, s0 + UR);
-    consume(va, s0);
-    load_batch(va, s0 + 2 * UR);
-    consume(vb, s0 + UR);
+  // Exactly the batches that hold rows are loaded, each issued one batch
+  // ahead: the main loop runs while two more batches follow, and the tail
+  // (one or two batches) is straight-line code, so every wait before a
+  // consume() leaves the next batch in flight and nothing is outstanding at
+  // the end.
+  const int nb = any_rows ? (steps + UR - 1) / UR : 0;
+  int bi = 0;
+  for (; bi + 2 < nb; bi += 2) {
+    load_batch(vb, (bi + 1) * UR);
+    consume(va, bi * UR);
+    load_batch(va, (bi + 2) * UR);
+    consume(vb, (bi + 1) * UR);
+  }
+  if (nb - bi == 2) {
+    load_batch(vb, (bi + 1) * UR);
+    consume(va, bi * UR);
+    consume(vb, (bi + 1) * UR);
+  } else if (nb - bi == 1) {
+    consume(va, bi * UR);
   }
 
   return true;
@@ -418,21 +430,21 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
 // single chunk -- the keys are in LDS; several chunks -- the last chunk of
 // (b, g) to arrive reads the published scores.  Returns true in the
 // workgroup that selected.
-template <int NT, bool PUB>
-__device__ __forceinline__ bool select_scored(const ScoreParams& p, int g, int b, uint32_t* smem,
-                                              TopkShared<NT>& sh, int* s_flag) {
+// nc: the candidates of sequence b, k: its k (both as read by the caller).
+// SINGLE: compiled for the single-chunk mode only.
+template <int NT, bool PUB, bool SINGLE = false>
+__device__ __forceinline__ bool select_scored(const ScoreParams& p, int g, int b, int nc, int k,
+                                              uint32_t* smem, TopkShared<NT>& sh, int* s_flag) {
   const int T = p.T;
-  const int nc = n_candidates(p.seq_lens[b], p.window, p.blk);
   const int nchunks = max(1, (nc + p.rows_per_chunk - 1) / p.rows_per_chunk);
   uint32_t* keys = smem + T * p.D;
   int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + T * p.score_cols);
   float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
   const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
-  const int k = p.k_per_seq[b];
   int32_t* idx_out = p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max;
   int32_t* nsel_out = p.n_sel + (int64_t)b * T * p.Hkv + g;
   float* ov_out = p.overlap ? p.overlap + b * p.Hkv + g : nullptr;
-  if (p.single_chunk) {
+  if (SINGLE || p.single_chunk) {
     lds_barrier();
     select_rows<NT, PUB>(nullptr, 0, false, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
                          (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
@@ -455,7 +467,8 @@ __device__ __forceinline__ bool score_task(const ScoreParams& p, int c, int g, i
                                            TopkShared<NT>& sh, int* s_flag) {
   if (!score_rows<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, smem)) return false;
   if (!p.fused_select) return false;
-  return select_scored<NT, PUB>(p, g, b, smem, sh, s_flag);
+  return select_scored<NT, PUB>(p, g, b, n_candidates(p.seq_lens[b], p.window, p.blk), p.k_per_seq[b],
+                                smem, sh, s_flag);
 }
 
 }  // namespace skv

@@ -40,8 +40,9 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   const int L = a.seq_lens[b];
   const int ws = L - a.window > 0 ? L - a.window : 0;
   const int nc = n_candidates(L, a.window, a.blk);
+  const int k = s.k_per_seq[b];
   // the selection returns clamp(min(k, candidates), 0, k_max) blocks
-  int nsel = min(s.k_per_seq[b], nc);
+  int nsel = min(k, nc);
   nsel = max(0, min(nsel, a.k_max));
   const int nwin_items = window_blocks(a, L, ws) * C::SUB;
   const int count = nwin_items + nsel * C::SUB;
@@ -55,8 +56,8 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
         return describe_sparse<KV, D, BLK>(a, b, g, m, lds_idx[m], -1, (item - nwin_items) % C::SUB);
       },
       [&](int item) { return item < nwin_items; },
-      [&] { (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR>(s, 0, g, b, score_smem); },
-      [&] { (void)select_scored<kPairThreads, false>(s, g, b, score_smem, sh, &s_flag); });
+      [&] { (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem); },
+      [&] { (void)select_scored<kPairThreads, false, true>(s, g, b, nc, k, score_smem, sh, &s_flag); });
   attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag, nullptr);
 }
 
