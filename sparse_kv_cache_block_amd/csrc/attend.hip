@@ -23,7 +23,8 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   const int count = max(0, min(p.items_per_split, total - first));
   attend_items<KV, D, BLK, kAttnWaves>(
       p, smem, b, g, first, count, [&](int item) { return describe<KV, D, BLK>(p, b, g, item, nsel, ws); },
-      [](int) { return true; }, [] {}, [] {});
+      [](int) { return ItemDesc{0, 0, 0}; }, [](int) { return true; },
+      [](auto&& issue_first) { issue_first(); }, [] {});
   attend_finish<KV, D, BLK, kAttnWaves>(p, smem, b, g, split, p.n_splits, &s_last, nullptr);
 }
 

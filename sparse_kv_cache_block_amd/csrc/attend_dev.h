@@ -60,10 +60,13 @@ struct AttnCfg {
 };
 
 // Descriptor of one item, held by one lane of the wave that processes it.
+// It keeps the block's row in its source as loaded (no arithmetic on it), so
+// building a descriptor never waits for a table lookup; the element offset
+// and the fp8 scales are formed when the item's loads are issued.
 struct ItemDesc {
-  int64_t off;    // element offset of the item's first row in its K/V arrays
+  int row;        // physical block (paged source), staging slot, or first token row (window buffer)
   int pos0;       // sequence position of the item's row 0; bit 31 marks a window item
-  float ks, vs;   // fp8 scales
+  int sub;        // slice of the block
 };
 
 // Slice `sub` of the m-th selected block of (b, g), block id j.  A paged
@@ -74,25 +77,12 @@ __device__ __forceinline__ ItemDesc describe_sparse(const AttnParams& p, int b, 
                                                     int64_t phys, int sub) {
   using C = AttnCfg<KV, D, BLK>;
   ItemDesc d;
-  d.ks = 1.f;
-  d.vs = 1.f;
+  d.sub = sub;
   d.pos0 = j * BLK + sub * C::TB;
-  if (p.sparse_kind == SKV_SRC_PAGED) {
-    if (phys < 0) phys = p.block_table[(int64_t)b * p.max_blocks + j];
-    d.off = phys * p.stride_block + (int64_t)g * p.stride_head;
-    if (KV == KV_FP8) {
-      d.ks = p.sks[phys * p.Hkv + g];
-      d.vs = p.svs[phys * p.Hkv + g];
-    }
-  } else {
-    const int64_t slot = ((int64_t)b * p.Hkv + g) * p.k_max + m;
-    d.off = slot * BLK * D;
-    if (KV == KV_FP8) {
-      d.ks = p.sks[slot];
-      d.vs = p.svs[slot];
-    }
-  }
-  d.off += (int64_t)sub * C::TB * D;
+  if (p.sparse_kind == SKV_SRC_PAGED)
+    d.row = phys >= 0 ? (int)phys : p.block_table[(int64_t)b * p.max_blocks + j];
+  else
+    d.row = (b * p.Hkv + g) * p.k_max + m;
   return d;
 }
 
@@ -101,23 +91,16 @@ template <int KV, int D, int BLK>
 __device__ __forceinline__ ItemDesc describe_window(const AttnParams& p, int b, int g, int c, int sub, int ws) {
   using C = AttnCfg<KV, D, BLK>;
   ItemDesc d;
-  d.ks = 1.f;
-  d.vs = 1.f;
+  d.sub = sub;
   if (p.window_kind == SKV_SRC_PAGED) {
     const int j = ws / BLK + c;
     d.pos0 = j * BLK + sub * C::TB;
-    const int64_t phys = p.window_table[(int64_t)b * p.max_blocks + j];
-    d.off = phys * p.stride_block + (int64_t)g * p.stride_head;
-    if (KV == KV_FP8) {
-      d.ks = p.wks[phys * p.Hkv + g];
-      d.vs = p.wvs[phys * p.Hkv + g];
-    }
+    d.row = p.window_table[(int64_t)b * p.max_blocks + j];
   } else {
     d.pos0 = ws + c * BLK + sub * C::TB;
-    d.off = (((int64_t)b * p.Hkv + g) * p.window + (int64_t)c * BLK) * D;
+    d.row = (b * p.Hkv + g) * p.window + c * BLK;
   }
   d.pos0 |= (int)0x80000000;
-  d.off += (int64_t)sub * C::TB * D;
   return d;
 }
 
@@ -148,17 +131,22 @@ __device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws)
 }
 
 // One NW-wave workgroup's attention of (b, g) over items [first, first+count)
-// of a list described by desc(item).  Wave w takes items first + w,
-// first + w + NW, ...; lane j of the wave holds the descriptor of the wave's
-// j-th item.  Items for which early(item) holds are described up front; the
-// others only after the hooks: pre() runs once the query loads are issued,
-// then each wave whose first item is early issues that item's loads, then
-// post() runs (both hooks run in every thread).  Leaves each wave's
-// unnormalised O rows, running max and sum in its LDS combine region.
-template <int KV, int D, int BLK, int NW, class DescFn, class EarlyFn, class PreFn, class PostFn>
+// of its list.  Wave w takes items first + w, first + w + NW, ...; lane j of
+// the wave holds the descriptor of the wave's j-th item.  Items for which
+// early(item) holds are described by desc_early before the hooks, the others
+// by desc_late after them; both are called for every lane with an item of
+// the list (clamped), so they must accept any of them.  pre(issue_first) runs
+// once the query loads are issued and must call issue_first() exactly once,
+// which issues the loads of the wave's first item if that item is early (a
+// wave without one issues the same loads from row 0 of its source, so every
+// path has the same count of loads in flight); post() runs after pre (both
+// hooks run in every thread).  Leaves each wave's unnormalised O rows,
+// running max and sum in its LDS combine region.
+template <int KV, int D, int BLK, int NW, class EarlyDescFn, class LateDescFn, class EarlyFn, class PreFn,
+          class PostFn>
 __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, int b, int g, int first,
-                                             int count, DescFn desc, EarlyFn early, PreFn pre,
-                                             PostFn post) {
+                                             int count, EarlyDescFn desc_early, LateDescFn desc_late,
+                                             EarlyFn early, PreFn pre, PostFn post) {
   using C = AttnCfg<KV, D, BLK>;
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15;   // C/B column, A row
@@ -192,13 +180,13 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   }
 
   const int my_items = count > w ? (count - w + NW - 1) / NW : 0;  // this wave's items
-  const int my_item = first + w + NW * lane;
+  const int my_item = min(first + w + NW * lane, first + count - 1);
 
   // lane j describes this wave's item j; early and late descriptors stay in
   // separate registers, so reading an early item never waits for the loads
   // behind a late one
-  ItemDesc d_early{0, 0, 1.f, 1.f}, d_late{0, 0, 1.f, 1.f};
-  if (lane < my_items && early(my_item)) d_early = desc(my_item);
+  ItemDesc d_early{0, 0, 0}, d_late{0, 0, 0};
+  if (count > 0) d_early = desc_early(my_item);
 
   const char* kbase_s = static_cast<const char*>(p.sk);
   const char* vbase_s = static_cast<const char*>(p.sv);
@@ -216,20 +204,24 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   int pos0 = 0;
   float ksc = 1.f, vsc = 1.f;
 
-  // Issue the loads of item j (descriptor broadcast from lane j).
-  auto read_desc = [&](const ItemDesc& d, int j, int64_t& off) {
-    const int lo32 = __builtin_amdgcn_readlane((int)(uint32_t)d.off, j);
-    const int hi32 = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)d.off >> 32), j);
-    off = (int64_t)(((uint64_t)(uint32_t)hi32 << 32) | (uint32_t)lo32);
-    pos0 = __builtin_amdgcn_readlane(d.pos0, j);
-    ksc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d.ks), j));
-    vsc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(d.vs), j));
-  };
-  auto load_item = [&](int j) {
-    int64_t off;
-    if (early(first + w + NW * j)) read_desc(d_early, j, off);   // uniform branch
-    else read_desc(d_late, j, off);
+  // Issue the loads of the slice `sub` of `row` (pos0 already set).
+  auto issue = [&](int row, int sub) {
+    // element offset of the slice, and its fp8 scales, from the source kind
     const bool win = pos0 < 0;
+    const int kind = win ? p.window_kind : p.sparse_kind;
+    int64_t off;
+    if (kind == SKV_SRC_PAGED) off = (int64_t)row * p.stride_block + (int64_t)g * p.stride_head;
+    else if (kind == SKV_SRC_STAGED) off = (int64_t)row * BLK * D;
+    else off = (int64_t)row * D;
+    off += (int64_t)sub * C::TB * D;
+    if constexpr (KV == KV_FP8) {
+      // paged: per (block, head) scales; staged: per slot (fp8 window buffers are rejected)
+      if (kind != SKV_SRC_WINDOW) {
+        const int64_t si = kind == SKV_SRC_PAGED ? (int64_t)row * p.Hkv + g : row;
+        ksc = (win ? p.wks : p.sks)[si];
+        vsc = (win ? p.wvs : p.svs)[si];
+      }
+    }
     const char* kb = (win ? kbase_w : kbase_s) + off * C::ES;
     const char* vb = (win ? vbase_w : vbase_s) + off * C::ES;
 #pragma unroll
@@ -241,12 +233,27 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
 #pragma unroll
     for (int i = 0; i < C::NV; ++i) vr[i] = load_stream16(vb + 16 * (lane + kWave * i));
   };
+  // Issue the loads of the wave's item j (descriptor broadcast from lane j;
+  // scalar selects between the early and late descriptors).
+  auto load_item = [&](int j) {
+    const bool e = early(first + w + NW * j);
+    const int re = __builtin_amdgcn_readlane(d_early.row, j), rl = __builtin_amdgcn_readlane(d_late.row, j);
+    const int pe = __builtin_amdgcn_readlane(d_early.pos0, j), pl = __builtin_amdgcn_readlane(d_late.pos0, j);
+    const int se = __builtin_amdgcn_readlane(d_early.sub, j), sl = __builtin_amdgcn_readlane(d_late.sub, j);
+    pos0 = e ? pe : pl;
+    issue(e ? re : rl, e ? se : sl);
+  };
 
-  pre();
   const bool first_early = my_items > 0 && early(first + w);
-  if (first_early) load_item(0);
+  pre([&] {
+    const int r0 = __builtin_amdgcn_readlane(d_early.row, 0);
+    const int s0 = __builtin_amdgcn_readlane(d_early.sub, 0);
+    const int p0 = __builtin_amdgcn_readlane(d_early.pos0, 0);
+    pos0 = first_early ? p0 : 0;
+    issue(first_early ? r0 : 0, first_early ? s0 : 0);
+  });
   post();
-  if (lane < my_items && !early(my_item)) d_late = desc(my_item);
+  if (count > 0) d_late = desc_late(my_item);
   if (my_items > 0 && !first_early) load_item(0);
 
   for (int j = 0; j < my_items; ++j) {

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkParams p) {
   uint32_t* keys = smem;
   int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + p.max_blocks);
   const int64_t t_stride = (int64_t)p.Hkv * p.max_blocks;
-  select_rows<kSelThreads, false>(p.scores + ((int64_t)b * p.T * p.Hkv + g) * p.max_blocks, t_stride, false, keys, 0, nc,
+  (void)select_rows<kSelThreads, false>(p.scores + ((int64_t)b * p.T * p.Hkv + g) * p.max_blocks, t_stride, false, keys, 0, nc,
               p.T, p.k_per_seq[b], p.k_max, p.indices + ((int64_t)b * p.T * p.Hkv + g) * p.k_max,
               (int64_t)p.Hkv * p.k_max, p.n_sel + (int64_t)b * p.T * p.Hkv + g, p.Hkv,
               p.overlap ? p.overlap + b * p.Hkv + g : nullptr, lds_idx, sh);

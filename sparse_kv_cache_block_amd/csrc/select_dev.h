@@ -79,8 +79,9 @@ __device__ __forceinline__ void put_f32(float* p, float v) {
 }
 
 // Select the k largest of keys[0..n) (ties to the lowest index).  Writes the
-// chosen indices in ascending order to out[0..k') and -1 to out[k'..k_max);
-// mirrors them to lds_out.  Returns k' = clamp(min(k, n), 0, k_max).
+// chosen indices in ascending order to lds_out[0..k') and -1 to
+// lds_out[k'..k_max), and the same to out unless it is null.  Returns
+// k' = clamp(min(k, n), 0, k_max).
 //
 // Radix select on 8-bit digits, most significant first: each pass builds the
 // histogram of the digit among the keys that match the known prefix, one wave
@@ -153,7 +154,7 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
   const uint32_t ex = block_exclusive_scan<NT>((gt << 16) | eq, sh.scan_w[0], tot);
   if (take_all) {
     for (int j = j0; j < j1; ++j) {
-      put_i32<PUB>(out + j, j);
+      if (out) put_i32<PUB>(out + j, j);
       lds_out[j] = j;
     }
   } else if (kk > 0) {
@@ -168,7 +169,7 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
         ++eq_seen;
       }
       if (keep) {
-        put_i32<PUB>(out + pos, j);
+        if (out) put_i32<PUB>(out + pos, j);
         lds_out[pos] = j;
         ++pos;
       }
@@ -176,7 +177,7 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
   }
   const int nsel = take_all ? n : kk;
   for (int m = nsel + tid; m < k_max; m += NT) {
-    put_i32<PUB>(out + m, -1);
+    if (out) put_i32<PUB>(out + m, -1);
     lds_out[m] = -1;
   }
   lds_barrier();  // scan buffer and lds_out are reused by the caller
@@ -230,9 +231,12 @@ __device__ __forceinline__ void load_keys(const float* row, int nc, bool coheren
 
 // Selection for one (b, g) and every query token.  Token t's keys are at
 // keys + t * key_stride (already there when `scores` is null, else loaded
-// from scores + t * t_stride).
+// from scores + t * t_stride).  Token t's ids go to lds_idx + t * k_max and,
+// unless the pointers are null, to the global index and count rows.  Returns
+// the overlap of the two tokens' lists (1 with one token), also written to
+// overlap_out unless it is null.
 template <int NT, bool PUB>
-__device__ __forceinline__ void select_rows(const float* scores, int64_t t_stride, bool coherent,
+__device__ __forceinline__ float select_rows(const float* scores, int64_t t_stride, bool coherent,
                                             uint32_t* keys, int key_stride, int nc, int T, int k,
                                             int k_max, int32_t* indices, int64_t idx_t_stride,
                                             int32_t* n_sel, int64_t nsel_t_stride, float* overlap_out,
@@ -246,13 +250,15 @@ __device__ __forceinline__ void select_rows(const float* scores, int64_t t_strid
     }
     const int ns = block_select<NT, PUB>(kt, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
     if (t == 0) ns0 = ns; else ns1 = ns;
-    if (threadIdx.x == 0) put_i32<PUB>(n_sel + t * nsel_t_stride, ns);
+    if (n_sel && threadIdx.x == 0) put_i32<PUB>(n_sel + t * nsel_t_stride, ns);
     lds_barrier();
   }
-  if (T == 2 && overlap_out) {
-    const float ov = list_overlap<NT>(lds_idx, ns0, lds_idx + k_max, ns1, sh);
-    if (threadIdx.x == 0) put_f32<PUB>(overlap_out, ov);
+  float ov = 1.0f;
+  if (T == 2) {
+    ov = list_overlap<NT>(lds_idx, ns0, lds_idx + k_max, ns1, sh);
+    if (overlap_out && threadIdx.x == 0) put_f32<PUB>(overlap_out, ov);
   }
+  return ov;
 }
 
 // Physical block of every selected index (row b of the block table).
@@ -446,12 +452,12 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int g, int b
   float* ov_out = p.overlap ? p.overlap + b * p.Hkv + g : nullptr;
   if (SINGLE || p.single_chunk) {
     lds_barrier();
-    select_rows<NT, PUB>(nullptr, 0, false, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
+    (void)select_rows<NT, PUB>(nullptr, 0, false, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
                          (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
   } else {
     // ---- several chunks: the last one of (b, g) to arrive selects
     if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, s_flag)) return false;
-    select_rows<NT, PUB>(sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
+    (void)select_rows<NT, PUB>(sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
                          (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
   }
   if (p.phys)

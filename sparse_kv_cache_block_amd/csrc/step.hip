@@ -6,12 +6,16 @@
 // The window part does not depend on the selection (Beyond abstract: the
 // recent window is attended densely, the older entries sparsely per head), so
 // the workgroup's item list puts the window slices first and each wave issues
-// the loads of its first window slice before the selection starts: the radix
-// select runs in LDS while those loads are in flight, and its barriers wait
-// for LDS traffic only.  The window descriptors and the attention's query
+// the loads of its first window slice as soon as its scoring is done: the
+// radix select runs in LDS while those loads are in flight, and its barriers
+// wait for LDS traffic only.  The window descriptors and the attention's query
 // operand are loaded before the scoring; the sparse descriptors (block ids from
 // the selection in LDS, physical ids from the block table) after it, while the
 // waves work through their window slices.
+//
+// The selection stays in LDS until the attention is done (global stores
+// issued during the select would queue behind the window loads), and the
+// selected ids, counts and the dual-query overlap are written at the end.
 //
 // The arithmetic of every phase is that of the stand-alone kernels
 // (select_dev.h, attend_dev.h).  One workgroup owns a pair, so there is a
@@ -46,19 +50,47 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   nsel = max(0, min(nsel, a.k_max));
   const int nwin_items = window_blocks(a, L, ws) * C::SUB;
   const int count = nwin_items + nsel * C::SUB;
-  const int32_t* lds_idx = reinterpret_cast<const int32_t*>(score_smem + s.T * D + s.T * s.score_cols);
+  uint32_t* keys = score_smem + s.T * D;
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + s.T * s.score_cols);
+  float overlap = 1.0f;
 
   attend_items<KV, D, BLK, kPairWaves>(
       a, smem, b, g, 0, count,
+      // window slices first (clamped for lanes past them) ...
       [&](int item) {
-        if (item < nwin_items) return describe_window<KV, D, BLK>(a, b, g, item / C::SUB, item % C::SUB, ws);
-        const int m = (item - nwin_items) / C::SUB;
-        return describe_sparse<KV, D, BLK>(a, b, g, m, lds_idx[m], -1, (item - nwin_items) % C::SUB);
+        if (nwin_items == 0) return ItemDesc{0, 0, 0};
+        const int it = min(item, nwin_items - 1);
+        return describe_window<KV, D, BLK>(a, b, g, it / C::SUB, it % C::SUB, ws);
+      },
+      // ... then the selected blocks, described once the selection is in LDS
+      [&](int item) {
+        if (nsel == 0) return ItemDesc{0, 0, 0};
+        const int it = max(item - nwin_items, 0);
+        const int m = min(it / C::SUB, nsel - 1);
+        return describe_sparse<KV, D, BLK>(a, b, g, m, lds_idx[m], -1, it % C::SUB);
       },
       [&](int item) { return item < nwin_items; },
-      [&] { (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem); },
-      [&] { (void)select_scored<kPairThreads, false, true>(s, g, b, nc, k, score_smem, sh, &s_flag); });
+      [&](auto&& issue_first) {
+        (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem);
+        issue_first();
+      },
+      [&] {
+        // the selection stays in LDS here: global stores would queue behind
+        // the window loads just issued
+        lds_barrier();
+        overlap = select_rows<kPairThreads, false>(nullptr, 0, false, keys, s.score_cols, nc, s.T, k, s.k_max,
+                                                   nullptr, 0, nullptr, 0, nullptr, lds_idx, sh);
+      });
   attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag, nullptr);
+
+  // ---- the selection's outputs: ids (-1 past the count), counts, overlap
+  const int T = s.T;
+  for (int i = threadIdx.x; i < T * s.k_max; i += kPairThreads) {
+    const int t = i / s.k_max, m = i % s.k_max;
+    s.indices[(((int64_t)b * T + t) * s.Hkv + g) * s.k_max + m] = lds_idx[i];
+  }
+  if (threadIdx.x < T) s.n_sel[((int64_t)b * T + threadIdx.x) * s.Hkv + g] = nsel;
+  if (T == 2 && s.overlap && threadIdx.x == 0) s.overlap[b * s.Hkv + g] = overlap;
 }
 
 bool step_kernel_available(const skv_problem& p) {
