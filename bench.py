@@ -2,16 +2,17 @@
 """Benchmark of the sparse-KV decode step on one MI355X.
 
 A step is one pass of the whole hot path -- landmark scoring, per-KV-head
-top-k, the paged gather fused into the attention loads, split-K attention over
-the selected blocks plus the recent window, and the log-sum-exp merge -- over
-one batch of seeded synthetic inputs already resident in HBM.  Steps rotate
-over several independent input instances so that neither the landmarks nor
-the K/V blocks can be served from the 256 MB last-level cache between steps.
+top-k, the paged gather fused into the attention loads, attention over the
+selected blocks plus the recent window, and the log-sum-exp merge -- over one
+batch of seeded synthetic inputs already resident in HBM.  Steps rotate over
+several independent input instances so that neither the landmarks nor the K/V
+blocks can be served from the 256 MB last-level cache between steps.
 
 Prints one JSON line: tokens/s (real query tokens per second), the dominant
-kernel's roofline (attention, algorithmic HBM bytes per launch over its mean
-launch time from HIP events on the launch stream), and the CPU oracle timed on
-a bounded sample of the same workload.
+kernel's roofline (algorithmic HBM bytes per launch over its mean launch time
+from HIP events on the launch stream: the single-launch step kernel where the
+step is one launch, else the attention launch timed alone), and the CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -49,30 +50,33 @@ def attention_bytes(wl, seq_lens, nsel_real) -> int:
     return total
 
 
-KERNEL_SOURCES = ("attend.hip", "skv_device.h", "skv_internal.h")
+KERNEL_SOURCES = {
+    "pair_step_kernel": ("step.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
+    "attend_kernel": ("attend.hip", "attend_dev.h", "skv_device.h", "skv_internal.h"),
+}
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the attention kernel's sources (counter results go stale when it changes)."""
+def kernel_source_digest(kernel: str) -> str:
+    """sha256 over a kernel's sources (counter results go stale when they change)."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sparse_kv_cache_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
-    """Per-launch HBM bytes of the attention kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"attend_kernel_{workload}_traffic.md")
+def recorded_traffic(kernel: str, workload: str):
+    """Per-launch HBM bytes of a kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     if "```json" not in text:
         return None
     rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
-    if rec.get("source_sha256") != kernel_source_digest():
+    if rec.get("source_sha256") != kernel_source_digest(kernel):
         return None
     return rec
 
@@ -176,44 +180,47 @@ def main() -> int:
     step_bytes = configs.algorithmic_bytes(wl, lens, kps)
     tokens_per_s = wl.batch * n_layers / (ms_per_step * 1e-3)
 
-    # ---- dominant kernel: the attention launch, timed alone over the same instances
-    attn_ms = None
-    attn_bytes = None
-    if wl.pool != "host":
-        launches = []
+    # ---- dominant kernel: the step itself when it is one launch, else the
+    # attention launch timed alone over the same instances
+    launches = B.sparsekv_decode_step_launches(steps[0].pr)
+    kernel = k_ms = k_bytes = None
+    if launches == 1:
+        kernel, k_ms, k_bytes = "pair_step_kernel", ms_per_step, step_bytes
+    elif wl.pool != "host":
+        sources = []
         for st in steps:
             d = st.inp
             sparse = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
-            launches.append((st, sparse))
+            sources.append((st, sparse))
         for k in range(args.warmup):
-            st, sp = launches[k % len(launches)]
+            st, sp = sources[k % len(sources)]
             B.sparsekv_attend(st.pr, st.inp.q, sp, st.indices, st.n_sel, sp, st.inp.seq_lens,
                               st.out, st.lse, st.ws)
         torch.cuda.synchronize()
         ev0.record(stream)
         for k in range(args.steps):
-            st, sp = launches[k % len(launches)]
+            st, sp = sources[k % len(sources)]
             B.sparsekv_attend(st.pr, st.inp.q, sp, st.indices, st.n_sel, sp, st.inp.seq_lens,
                               st.out, st.lse, st.ws)
         ev1.record(stream)
         ev1.synchronize()
-        attn_ms = ev0.elapsed_time(ev1) / args.steps
+        k_ms = ev0.elapsed_time(ev1) / args.steps
         per_inst = [attention_bytes(wl, s.inp.seq_lens.cpu().numpy(), s.n_sel[:, 0].cpu().numpy())
                     for s in steps]
-        attn_bytes = statistics.mean(per_inst)
-        log(f"attention kernel alone: {attn_ms * 1e3:.1f} us, {attn_bytes / 1e6:.1f} MB")
+        kernel, k_bytes = "attend_kernel", statistics.mean(per_inst)
+        log(f"attention kernel alone: {k_ms * 1e3:.1f} us, {k_bytes / 1e6:.1f} MB")
 
     roofline = None
-    if attn_ms:
-        achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
-        rec = recorded_traffic(wl.name)
+    if kernel:
+        achieved = k_bytes / (k_ms * 1e-3) / 1e9
+        rec = recorded_traffic(kernel, wl.name)
         traffic = None
         if rec is not None:
             traffic = int(rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"])
-        roofline = {"bound": "hbm", "kernel": "attend_kernel", "achieved": round(achieved, 1),
+        roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "bytes_per_launch": int(attn_bytes),
-                    "us_per_launch": round(attn_ms * 1e3, 2)}
+                    "traffic": traffic, "bytes_per_launch": int(k_bytes),
+                    "us_per_launch": round(k_ms * 1e3, 2)}
 
     # ---- CPU oracle on a bounded sample of instance 0
     cpu = None
@@ -264,6 +271,7 @@ def main() -> int:
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBS, 4),
         "wall_ms_per_step": round(wall_ms, 5),
+        "launches_per_step": launches,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

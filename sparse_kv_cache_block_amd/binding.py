@@ -25,7 +25,7 @@ DTYPE_CODE = {"fp32": SKV_F32, "bf16": SKV_BF16, "fp8": SKV_FP8_E4M3FN}
 EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_workspace_size", "sparsekv_workspace_init", "sparsekv_score",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
-            "sparsekv_decode_layers")
+            "sparsekv_decode_layers", "sparsekv_decode_step_launches")
 
 
 class SkvError(RuntimeError):
@@ -138,6 +138,12 @@ def sparsekv_version() -> str:
 def sparsekv_workspace_size(pr: Problem) -> int:
     n = C.c_size_t(0)
     _check(lib().sparsekv_workspace_size(C.byref(pr), C.byref(n)), "sparsekv_workspace_size")
+    return int(n.value)
+
+
+def sparsekv_decode_step_launches(pr: Problem) -> int:
+    n = C.c_int32(0)
+    _check(lib().sparsekv_decode_step_launches(C.byref(pr), C.byref(n)), "sparsekv_decode_step_launches")
     return int(n.value)
 
 

@@ -425,6 +425,14 @@ skv_status sparsekv_workspace_size(const skv_problem* pr, size_t* bytes) {
   return SKV_OK;
 }
 
+skv_status sparsekv_decode_step_launches(const skv_problem* pr, int32_t* launches) {
+  SKV_TRY(check_problem(pr));
+  if (!launches) return fail(SKV_E_NULL, "launches is NULL");
+  if (pr->pool_location == SKV_POOL_HOST) *launches = 3;
+  else *launches = make_plan(*pr).fused_step ? 1 : 2;
+  return SKV_OK;
+}
+
 skv_status sparsekv_workspace_init(void* workspace, size_t bytes, void* stream) {
   if (!workspace) return fail(SKV_E_NULL, "workspace is NULL");
   SKV_TRY_HIP(launch_fill_zero(workspace, bytes, as_stream(stream)), "workspace fill");

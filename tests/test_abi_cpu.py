@@ -57,6 +57,21 @@ def test_workspace_size_is_host_only(lib):
     assert B.sparsekv_version().count(".") == 2
 
 
+def test_decode_step_launch_count(lib):
+    # one launch for the 32k Llama-shaped layer (256 pairs), two when the
+    # pairs are too few to fill the chip or the shape has no step kernel,
+    # three for a host pool
+    big = dict(B=32, Hq=32, Hkv=8, max_blocks=1024, n_pool_blocks=32 * 1024, window=512, k_max=64)
+    assert B.sparsekv_decode_step_launches(_good_problem(**big)) == 1
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, kv_dtype="fp8"))) == 1
+    assert B.sparsekv_decode_step_launches(_good_problem()) == 2
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, d=64))) == 2
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, blk=16))) == 2
+    host = B.make_problem(32, 1, 32, 8, 128, 32, 1024, 32 * 1024, 8 * 32 * 128, 32 * 128, 512, 64,
+                          "bf16", "bf16", "bf16", pool_location=B.SKV_POOL_HOST)
+    assert B.sparsekv_decode_step_launches(host) == 3
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(Hq=6, Hkv=4), B.SKV_E_SHAPE),
     (dict(T=3), B.SKV_E_SHAPE),

@@ -155,6 +155,53 @@ def test_dual_identical_tokens_overlap_one():
     assert np.all(_np(st.overlap) == 1.0)
 
 
+# ------------------------------------------------ single-launch step (>= 128 pairs)
+# 16 sequences x 8 KV heads: decode_step runs as one launch, one workgroup per pair
+MIXED16 = [4096, 1000, 513, 37, 0, 1, 512, 513, 4000, 2048, 3333, 4095, 64, 700, 2500, 4096]
+
+
+def check_single_launch(wl, **kw):
+    inp, st = check_step(wl, **kw)
+    assert B.sparsekv_decode_step_launches(st.pr) == 1
+    return inp, st
+
+
+@pytest.mark.parametrize("kw,lens", [
+    (dict(), MIXED16),
+    (dict(window=0), None),                 # no window slice comes first in any wave
+    (dict(top_k=120), MIXED16),             # k beyond every sequence's candidates
+    (dict(block_size=64), MIXED16),
+    (dict(n_q_heads=16), None),             # G = 2
+    (dict(n_q_heads=64), None),             # G = 8
+])
+def test_single_launch_bf16(kw, lens):
+    args = dict(batch=16, context=4096)
+    args.update(kw)
+    check_single_launch(configs.LLAMA32K.scaled(**args), seq_lens=lens)
+
+
+def test_single_launch_ragged_poisoned():
+    check_single_launch(configs.RAGGED.scaled(batch=16, context=8192, ragged_min=100))
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(block_size=32, context=4096, window=256, top_k=20)])
+def test_single_launch_dual_fp8(kw):
+    args = dict(batch=16, context=8192, top_k=30)
+    args.update(kw)
+    check_single_launch(configs.DUAL.scaled(**args))
+
+
+def test_single_launch_ties():
+    def zero_q(inp):
+        inp.q.zero_()
+    inp, st = check_single_launch(configs.LLAMA32K.scaled(batch=16, context=4096), mutate=zero_q)
+    assert np.all(_np(st.indices)[:, 0, :, :] == np.arange(64)[None, None, :])
+
+    def dup(inp):
+        inp.landmarks[:, :, 1::2] = inp.landmarks[:, :, 0::2]
+    check_single_launch(configs.LLAMA32K.scaled(batch=16, context=4096, top_k=13), mutate=dup)
+
+
 # ------------------------------------------------------------ separate entry points
 def test_score_and_topk_entry_points():
     wl = configs.DUAL.scaled(batch=2, context=8192, top_k=40)
