@@ -13,7 +13,7 @@ namespace skv {
 
 constexpr int kSelThreads = 512;             // threads of the scoring / selection workgroups
 #ifndef SKV_SCORE_UR
-#define SKV_SCORE_UR 8
+#define SKV_SCORE_UR 4
 #endif
 
 // Grid (chunk, g, b); see score_task for the modes.

@@ -28,7 +28,7 @@ namespace skv {
 constexpr int kPairWaves = 8;
 constexpr int kPairThreads = kPairWaves * kWave;
 #ifndef SKV_PAIR_SCORE_UR
-#define SKV_PAIR_SCORE_UR 8
+#define SKV_PAIR_SCORE_UR 4
 #endif
 
 template <int KV, int BLK>
