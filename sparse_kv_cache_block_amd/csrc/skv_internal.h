@@ -75,6 +75,8 @@ struct AttnParams {
   unsigned* counters;       // [B][Hkv]
   float* out;               // [B][Hq][d]
   float* lse;               // [B][Hq] or null
+  int longest_first;        // single-launch step: workgroup row r takes the sequence of
+                            // length rank r (descending), so long pairs start first
 };
 
 // --------------------------------------------------------------------- gather

@@ -326,6 +326,10 @@ skv_status enqueue_step(const skv_problem& p, const Plan& pl, const skv_step_inp
   a.indices = out.indices;
   a.n_sel = out.n_sel;
   a.n_splits = 1;
+  int dev = 0, cus = 0;
+  SKV_TRY_HIP(hipGetDevice(&dev), "device query");
+  SKV_TRY_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "device query");
+  a.longest_first = p.batch * p.n_kv_heads > cus;
   SKV_TRY_HIP(launch_step(sp, a, pl.step_lds, s), "decode step launch");
   return SKV_OK;
 }

@@ -31,6 +31,29 @@ constexpr int kPairThreads = kPairWaves * kWave;
 #define SKV_PAIR_SCORE_UR 4
 #endif
 
+// The sequence whose length has rank r in descending order (ties to the lower
+// index).  Every wave computes it (scalar broadcasts of 64 lengths at a time),
+// so no barrier is needed.
+__device__ __forceinline__ int sequence_of_rank(const int32_t* seq_lens, int B, int r) {
+  const int lane = lane_id();
+  for (int c0 = 0; c0 < B; c0 += kWave) {
+    const int i = c0 + lane;
+    const int Li = i < B ? seq_lens[i] : -1;
+    int rank = 0;
+    for (int j0 = 0; j0 < B; j0 += kWave) {
+      const int Lj_lane = j0 + lane < B ? seq_lens[j0 + lane] : -1;
+      const int nj = min(kWave, B - j0);
+      for (int t = 0; t < nj; ++t) {
+        const int Lj = __builtin_amdgcn_readlane(Lj_lane, t);
+        rank += (Lj > Li || (Lj == Li && j0 + t < i)) ? 1 : 0;
+      }
+    }
+    const uint64_t hit = __ballot(i < B && rank == r);
+    if (hit) return c0 + (int)__builtin_ctzll(hit);
+  }
+  return r;
+}
+
 template <int KV, int BLK>
 __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, AttnParams a) {
   constexpr int D = 128;
@@ -40,7 +63,10 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   __shared__ TopkShared<kPairThreads> sh;
   __shared__ int s_flag;
 
-  const int g = blockIdx.x, b = blockIdx.y;
+  // workgroups start in row order: with more pairs than compute units, rows
+  // take the sequences longest first so the short pairs fill in at the end
+  const int g = blockIdx.x;
+  const int b = a.longest_first ? sequence_of_rank(a.seq_lens, a.B, blockIdx.y) : (int)blockIdx.y;
   const int L = a.seq_lens[b];
   const int ws = L - a.window > 0 ? L - a.window : 0;
   const int nc = n_candidates(L, a.window, a.blk);

@@ -180,6 +180,14 @@ def test_single_launch_bf16(kw, lens):
     check_single_launch(configs.LLAMA32K.scaled(**args), seq_lens=lens)
 
 
+def test_single_launch_longest_first():
+    # 40 x 8 = 320 pairs, more than the compute units: the step visits the
+    # sequences longest first; every output row must still be its own sequence's
+    lens = [int(x) for x in np.random.default_rng(7).integers(0, 2049, size=40)]
+    lens[3] = lens[4] = 2048   # equal lengths keep index order
+    check_single_launch(configs.LLAMA32K.scaled(batch=40, context=2048, top_k=24), seq_lens=lens)
+
+
 def test_single_launch_ragged_poisoned():
     check_single_launch(configs.RAGGED.scaled(batch=16, context=8192, ragged_min=100))
 
