@@ -64,7 +64,7 @@ template <int NT>
 struct TopkShared {
   uint32_t hist[2][256];
   uint32_t scan_w[2][NT / kWave];
-  uint32_t digit, above, common;
+  uint32_t digit, above, exact, common;
 };
 
 template <bool PUB>
@@ -81,16 +81,21 @@ __device__ __forceinline__ void put_f32(float* p, float v) {
 // Select the k largest of keys[0..n) (ties to the lowest index).  Writes the
 // chosen indices in ascending order to lds_out[0..k') and -1 to
 // lds_out[k'..k_max), and the same to out unless it is null.  Returns
-// k' = clamp(min(k, n), 0, k_max).
+// k' = clamp(min(k, n), 0, k_max).  hist0, when given, is the histogram of the
+// keys' top bytes (built while the keys were written); it replaces the first
+// pass's counting.
 //
 // Radix select on 8-bit digits, most significant first: each pass builds the
 // histogram of the digit among the keys that match the known prefix, one wave
 // finds the digit holding the k'-th largest key, and after four passes that
 // key T is known exactly.  Keys above T are all kept; keys equal to T are kept
-// in ascending index order until k' are chosen.
+// in ascending index order until k' are chosen.  A pass whose boundary digit
+// holds exactly the keys still needed ends the search early: the selection is
+// then every key at or above that prefix.
 template <int NT, bool PUB>
 __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, int k_max, int32_t* out,
-                                            int32_t* lds_out, TopkShared<NT>& sh) {
+                                            int32_t* lds_out, TopkShared<NT>& sh,
+                                            const uint32_t* hist0 = nullptr) {
   static_assert(NT >= 256, "the histogram is cleared by the first 256 threads");
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   int kk = k < n ? k : n;
@@ -100,16 +105,23 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
   uint32_t thresh = 0, take_eq = 0;
   if (!take_all && kk > 0) {
     uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kk;
-    if (tid < 256) sh.hist[0][tid] = 0;
-    lds_barrier();
+    bool at_or_above = false;
+    if (!hist0) {
+      if (tid < 256) sh.hist[0][tid] = 0;
+      lds_barrier();
+    }
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
-      uint32_t* hist = sh.hist[pass & 1];
-      for (int j = tid; j < n; j += NT) {
-        const uint32_t key = keys[j];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      const uint32_t* hist = sh.hist[pass & 1];
+      if (pass == 0 && hist0) {
+        hist = hist0;
+      } else {
+        for (int j = tid; j < n; j += NT) {
+          const uint32_t key = keys[j];
+          if ((key & pmask) == prefix) atomicAdd(&sh.hist[pass & 1][(key >> shift) & 255u], 1u);
+        }
+        lds_barrier();
       }
-      lds_barrier();
       if (w == 0) {
         // lane l owns digits 255-4l .. 252-4l (descending)
         uint32_t c[4], lsum = 0;
@@ -124,6 +136,7 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
           if (above < remaining && above + c[i] >= remaining) {
             sh.digit = 255u - 4 * lane - i;
             sh.above = above;
+            sh.exact = above + c[i] == remaining;
           }
           above += c[i];
         }
@@ -135,9 +148,13 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
       prefix |= sh.digit << shift;
       pmask |= 255u << shift;
       remaining -= sh.above;
+      if (sh.exact && prefix != 0u) {   // the whole boundary bin is taken
+        at_or_above = true;
+        break;
+      }
     }
-    thresh = prefix;
-    take_eq = remaining;
+    thresh = at_or_above ? prefix - 1u : prefix;
+    take_eq = at_or_above ? 0u : remaining;
   }
   // Emit in ascending index order: thread tid owns indices [j0, j1).
   const int per = (n + NT - 1) / NT;
@@ -234,13 +251,15 @@ __device__ __forceinline__ void load_keys(const float* row, int nc, bool coheren
 // from scores + t * t_stride).  Token t's ids go to lds_idx + t * k_max and,
 // unless the pointers are null, to the global index and count rows.  Returns
 // the overlap of the two tokens' lists (1 with one token), also written to
-// overlap_out unless it is null.
+// overlap_out unless it is null.  hist0, when given, holds each token's
+// top-byte key histogram (256 counts per token).
 template <int NT, bool PUB>
 __device__ __forceinline__ float select_rows(const float* scores, int64_t t_stride, bool coherent,
                                             uint32_t* keys, int key_stride, int nc, int T, int k,
                                             int k_max, int32_t* indices, int64_t idx_t_stride,
                                             int32_t* n_sel, int64_t nsel_t_stride, float* overlap_out,
-                                            int32_t* lds_idx, TopkShared<NT>& sh) {
+                                            int32_t* lds_idx, TopkShared<NT>& sh,
+                                            const uint32_t* hist0 = nullptr) {
   int ns0 = 0, ns1 = 0;
   for (int t = 0; t < T; ++t) {
     uint32_t* kt = keys + t * key_stride;
@@ -248,7 +267,8 @@ __device__ __forceinline__ float select_rows(const float* scores, int64_t t_stri
       load_keys<NT>(scores + t * t_stride, nc, coherent, kt);
       lds_barrier();
     }
-    const int ns = block_select<NT, PUB>(kt, nc, k, k_max, indices + t * idx_t_stride, lds_idx + t * k_max, sh);
+    const int ns = block_select<NT, PUB>(kt, nc, k, k_max, indices ? indices + t * idx_t_stride : nullptr,
+                                         lds_idx + t * k_max, sh, hist0 ? hist0 + t * 256 : nullptr);
     if (t == 0) ns0 = ns; else ns1 = ns;
     if (n_sel && threadIdx.x == 0) put_i32<PUB>(n_sel + t * nsel_t_stride, ns);
     lds_barrier();
@@ -309,6 +329,8 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
 
   float* qbar = reinterpret_cast<float*>(smem);  // [T][D]
   uint32_t* keys = smem + T * D;                 // [T][score_cols]
+  // LDS_KEYS: top-byte histogram of each token's keys, after the selected ids
+  uint32_t* hist0 = keys + T * p.score_cols + 2 * p.k_max;   // [2][256]
 
   const int lane = lane_id(), w = wave_id();
   const int sub = lane % LPR, rw = lane / LPR;
@@ -360,6 +382,9 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
       sum += h < p.G ? (Q_F32 ? __uint_as_float(qraw[h]) : __uint_as_float(qraw[h] << 16)) : 0.f;
     qbar[qi] = sum;
   }
+  if constexpr (LDS_KEYS) {
+    for (int i = threadIdx.x; i < 2 * 256; i += NT) hist0[i] = 0u;
+  }
   lds_barrier();
   float qr[2][EPL];
 #pragma unroll
@@ -398,7 +423,9 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
           float val = acc[t];
           if (val == 0.0f) val = 0.0f;  // one zero
           if (in_lds) {
-            keys[t * p.score_cols + r] = score_key(val);
+            const uint32_t key = score_key(val);
+            keys[t * p.score_cols + r] = key;
+            if constexpr (LDS_KEYS) atomicAdd(&hist0[t * 256 + (key >> 24)], 1u);
           } else {
             val = (r < nc) ? val : -INFINITY;
             if (p.fused_select) publish_f32(sc + t * t_stride + r, val);

@@ -125,10 +125,11 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 // LDS bytes of a scoring workgroup: qbar [T][d] floats, keys [T][score_cols]
-// (fused selection only) and the selected ids [2][k_max].
+// (fused selection only), the selected ids [2][k_max] and two 256-bin
+// top-byte key histograms.
 __host__ __device__ inline size_t score_lds_bytes(int T, int D, int score_cols, int k_max, bool fused) {
   size_t b = (size_t)T * D * 4;
-  if (fused) b += (size_t)T * score_cols * 4 + (size_t)2 * k_max * 4;
+  if (fused) b += (size_t)T * score_cols * 4 + (size_t)2 * k_max * 4 + (size_t)2 * 256 * 4;
   return b;
 }
 

@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
         // the window loads just issued
         lds_barrier();
         overlap = select_rows<kPairThreads, false>(nullptr, 0, false, keys, s.score_cols, nc, s.T, k, s.k_max,
-                                                   nullptr, 0, nullptr, 0, nullptr, lds_idx, sh);
+                                                   nullptr, 0, nullptr, 0, nullptr, lds_idx, sh,
+                                                   reinterpret_cast<const uint32_t*>(lds_idx + 2 * s.k_max));
       });
   attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag, nullptr);
 
