@@ -44,7 +44,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 template <int KV, int D, int BLK>
 struct AttnCfg {
   static constexpr int ES = KV == KV_F32 ? 4 : (KV == KV_BF16 ? 2 : 1);
-  static constexpr int TB = BLK < 32 ? BLK : 32;        // tokens per item
+  static constexpr int TB = attn_item_tokens(KV, BLK);  // tokens per item
   static constexpr int SUB = BLK / TB;                   // items per block
   static constexpr int NT = TB / 16;                     // QK tiles per item
   static constexpr int DT = D / 16;                      // PV output tiles
@@ -371,36 +371,41 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
             o[dt] = mfma_f32(a, *reinterpret_cast<const float*>(vrow + 64 * dt), o[dt]);
         }
     } else {
-      // P operand: element e of lane (n, kg) is token 4kg + e%4 of tile e/4
-      uint32_t pw[4];
+      // one MFMA per 32-token half of the item (two tiles)
+      constexpr int NH = (C::NT + 1) / 2;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        constexpr int NT = C::NT;
-        const int t0 = (2 * e2) / 4;
-        f32x2_t pv = {t0 < NT ? st[t0 < NT ? t0 : 0][(2 * e2) % 4] : 0.f,
-                      t0 < NT ? st[t0 < NT ? t0 : 0][(2 * e2 + 1) % 4] : 0.f};
-        if constexpr (KV == KV_FP8) pv *= vs_cur;
-        const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf16x2_t));
-        const f32x2_t rest = {pv.x - bf16_lo(hw), pv.y - bf16_hi(hw)};
-        const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_t));
-        pw[e2] = n < G ? hw : (n < ncols ? lw : 0u);
-      }
-      const uint4 aop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-      // B operand: lane r of row group kg reads row 4kg + r/4 (and +16), columns
-      // 16dt + 4(r%4) .. +3; the transposing read hands lane n column 16dt + n of
-      // those four rows, i.e. tokens 4kg .. 4kg+3 of each tile.
-      const char* tbase = vt + (4 * kg + (n >> 2)) * C::VROW + 8 * (n & 3);
+      for (int hh = 0; hh < NH; ++hh) {
+        // P operand: element e of lane (n, kg) is token 4kg + e%4 of tile 2hh + e/4
+        uint32_t pw[4];
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(tbase + 32 * dt));
-        i16x4_t hi4 = i16x4_t{0, 0, 0, 0};
-        if constexpr (C::NT > 1)
-          hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(tbase + 16 * C::VROW + 32 * dt));
-        const uint2 l2 = __builtin_bit_cast(uint2, lo4);
-        const uint2 h2 = __builtin_bit_cast(uint2, hi4);
-        o[dt] = mfma_bf16(aop, make_uint4(l2.x, l2.y, h2.x, h2.y), o[dt]);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          constexpr int NT = C::NT;
+          const int t0 = 2 * hh + (2 * e2) / 4;
+          const int tc = t0 < NT ? t0 : NT - 1;
+          f32x2_t pv = {t0 < NT ? st[tc][(2 * e2) % 4] : 0.f, t0 < NT ? st[tc][(2 * e2 + 1) % 4] : 0.f};
+          if constexpr (KV == KV_FP8) pv *= vs_cur;
+          const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf16x2_t));
+          const f32x2_t rest = {pv.x - bf16_lo(hw), pv.y - bf16_hi(hw)};
+          const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_t));
+          pw[e2] = n < G ? hw : (n < ncols ? lw : 0u);
+        }
+        const uint4 aop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        // B operand: lane r of row group kg reads row 32hh + 4kg + r/4 (and +16),
+        // columns 16dt + 4(r%4) .. +3; the transposing read hands lane n column
+        // 16dt + n of those four rows, i.e. tokens 4kg .. 4kg+3 of each tile.
+        const char* tbase = vt + (32 * hh + 4 * kg + (n >> 2)) * C::VROW + 8 * (n & 3);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(tbase + 32 * dt));
+          i16x4_t hi4 = i16x4_t{0, 0, 0, 0};
+          if (C::NT > 2 * hh + 1)
+            hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(tbase + 16 * C::VROW + 32 * dt));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo4);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi4);
+          o[dt] = mfma_bf16(aop, make_uint4(l2.x, l2.y, h2.x, h2.y), o[dt]);
+        }
       }
     }
     wave_lds_sync();

@@ -121,6 +121,10 @@ hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hi
 // Whether a step kernel is built for this shape (device pool, d = 128, bf16
 // queries and landmarks, bf16 or fp8 K/V, blocks of 32 or 64 tokens).
 bool step_kernel_available(const skv_problem& p);
+// Static LDS bytes of the step kernel for the problem's K/V type and block size.
+size_t step_static_lds_bytes(const skv_problem& p);
+// LDS of one compute unit on gfx950, the most one workgroup may use.
+constexpr size_t kLdsPerCu = 160 * 1024;
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 

@@ -120,7 +120,7 @@ Plan make_plan(const skv_problem& p) {
   pl.score_chunks = pl.max_cand > 0 ? (pl.max_cand + pl.rows_per_chunk - 1) / pl.rows_per_chunk : 1;
   // attention: items (32-token slices) of the sparse + window list per split,
   // aiming at about three resident workgroups per compute unit
-  const int sub = blk >= 32 ? blk / 32 : 1;
+  const int sub = blk / attn_item_tokens(kv_kind(p.kv_dtype), blk);
   const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
   const int total_items = (p.k_max + nwb) * sub;
   int ips = (int)(((int64_t)pairs * total_items + kAttnTargetWorkgroups - 1) / kAttnTargetWorkgroups);
@@ -135,7 +135,8 @@ Plan make_plan(const skv_problem& p) {
 #ifndef SKV_NO_STEP_KERNEL
   if (step_kernel_available(p) && pairs >= kStepMinPairs) {
     pl.step_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true);
-    pl.fused_step = pl.step_lds <= kStepMaxScoreLds;
+    pl.fused_step = pl.step_lds <= kStepMaxScoreLds &&
+                    step_static_lds_bytes(p) + pl.step_lds <= kLdsPerCu;
   }
 #endif
   size_t off = 0;

@@ -126,6 +126,15 @@ bool step_kernel_available(const skv_problem& p) {
          (p.block_size == 32 || p.block_size == 64);
 }
 
+size_t step_static_lds_bytes(const skv_problem& p) {
+  const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
+  const size_t attn = fp8 ? (p.block_size == 32 ? attn_lds_bytes<KV_FP8, 128, 32>(kPairWaves)
+                                                : attn_lds_bytes<KV_FP8, 128, 64>(kPairWaves))
+                          : (p.block_size == 32 ? attn_lds_bytes<KV_BF16, 128, 32>(kPairWaves)
+                                                : attn_lds_bytes<KV_BF16, 128, 64>(kPairWaves));
+  return attn + sizeof(TopkShared<kPairThreads>) + 16;
+}
+
 hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hipStream_t st) {
   const dim3 grid(a.Hkv, a.B);
   const dim3 block(kPairThreads);
