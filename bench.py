@@ -94,6 +94,25 @@ def copy_probe(mib: int, reps: int) -> int:
     return 0
 
 
+def h2d_ceiling_gbps(mib: int = 64, reps: int = 20) -> float:
+    """Contiguous host-to-device copy rate from pinned memory (hipMemcpyAsync
+    through torch), the reference for the host-link rate of the gather."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    e1.synchronize()
+    return n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +296,15 @@ def main() -> int:
     }
     if wl.n_q_tokens == 2:
         line["overlap_mean"] = round(float(steps[0].overlap.mean().item()), 4)
+    if wl.pool == "host":
+        # the gather's pull over the host link, against a contiguous pinned copy
+        link_bytes = n_layers * configs.host_link_bytes(wl, lens, kps)
+        link_gbps = link_bytes / (ms_per_step * 1e-3) / 1e9
+        ceiling = h2d_ceiling_gbps()
+        line["host_link"] = {"bytes_per_step": int(link_bytes), "gbps": round(link_gbps, 2),
+                             "h2d_ceiling_gbps": round(ceiling, 2), "frac": round(link_gbps / ceiling, 4),
+                             "note": "whole-step time (scoring and attention included) over the "
+                                     "gathered K/V bytes; ceiling = 64 MiB pinned hipMemcpyAsync"}
     print(json.dumps(line), flush=True)
     return 0
 
