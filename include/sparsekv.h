@@ -192,6 +192,37 @@ skv_status sparsekv_gather(const skv_problem *pr, const void *k_pool, const void
                            float *k_stage_scales, float *v_stage_scales, void *stream);
 
 /*
+ * Speculative prefetch correction (DualDecoder review, mechanism summary and
+ * Fig. 19: blocks are fetched early by the index predicted from a speculative
+ * token; once the real token's index is known the missing blocks are fetched
+ * and a GPU kernel reorders the staged blocks into the real index's order).
+ *
+ * spec_k_stage / spec_v_stage (and, for fp8, spec_k_scales / spec_v_scales)
+ * hold the gather of a speculative selection: slot m of row (b, g) holds
+ * block spec_indices[b, spec_token, g, m].  This call writes into k_stage /
+ * v_stage exactly the gather of the real selection -- byte for byte what
+ * sparsekv_gather writes for it: a real block that the speculative row also
+ * holds is copied from its speculative slot (device memory); the others, the
+ * misses, are read from the pool (over the host link for a pinned pool).
+ * Selections use the layouts sparsekv_topk writes ([B][T][Hkv][k_max] ids in
+ * ascending order within n_sel, n_sel [B][T][Hkv]); spec_* and real_* may be
+ * different arrays (the speculative one from an earlier step).  misses
+ * [B][Hkv] (may be NULL) receives, per row, how many real blocks were not in
+ * the speculative row.  The two stages must not overlap.  Slots >= n_sel of
+ * the real row are left untouched.
+ */
+skv_status sparsekv_gather_correct(const skv_problem *pr, const void *k_pool, const void *v_pool,
+                                   const float *k_scales, const float *v_scales,
+                                   const int32_t *block_table, const int32_t *spec_indices,
+                                   const int32_t *spec_n_sel, int32_t spec_token,
+                                   const void *spec_k_stage, const void *spec_v_stage,
+                                   const float *spec_k_scales, const float *spec_v_scales,
+                                   const int32_t *real_indices, const int32_t *real_n_sel,
+                                   int32_t real_token, void *k_stage, void *v_stage,
+                                   float *k_stage_scales, float *v_stage_scales, int32_t *misses,
+                                   void *stream);
+
+/*
  * Attention (attend step above) for the real token (t = 0) of every query
  * head h of group g:
  *   sparse part: positions p = j*blk + r of the selected blocks j with p < ws_b

@@ -25,7 +25,7 @@ DTYPE_CODE = {"fp32": SKV_F32, "bf16": SKV_BF16, "fp8": SKV_FP8_E4M3FN}
 EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_workspace_size", "sparsekv_workspace_init", "sparsekv_score",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
-            "sparsekv_decode_layers", "sparsekv_decode_step_launches")
+            "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct")
 
 
 class SkvError(RuntimeError):
@@ -83,6 +83,9 @@ def lib() -> C.CDLL:
             "sparsekv_score": (C.c_int, [P, vp, vp, vp, vp, vp]),
             "sparsekv_topk": (C.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
             "sparsekv_gather": (C.c_int, [P] + [vp] * 12),
+            "sparsekv_gather_correct": (C.c_int, [P] + [vp] * 7 + [C.c_int32] + [vp] * 6 + [C.c_int32]
+                                        + [vp] * 6),
+            "sparsekv_decode_step_launches": (C.c_int, [P, C.POINTER(C.c_int32)]),
             "sparsekv_attend": (C.c_int, [P, vp, C.POINTER(KvSource), vp, vp, C.POINTER(KvSource),
                                           vp, vp, vp, vp, sz, vp]),
             "sparsekv_decode_step": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
@@ -170,6 +173,19 @@ def sparsekv_gather(pr: Problem, k_pool, v_pool, k_scales, v_scales, block_table
                                  _ptr(v_scales), _ptr(block_table), _ptr(indices), _ptr(n_sel),
                                  _ptr(k_stage), _ptr(v_stage), _ptr(k_stage_scales),
                                  _ptr(v_stage_scales), _stream(stream)), "sparsekv_gather")
+
+
+def sparsekv_gather_correct(pr: Problem, k_pool, v_pool, k_scales, v_scales, block_table,
+                            spec_indices, spec_n_sel, spec_token: int, spec_k_stage, spec_v_stage,
+                            spec_k_scales, spec_v_scales, real_indices, real_n_sel, real_token: int,
+                            k_stage, v_stage, k_stage_scales=None, v_stage_scales=None, misses=None,
+                            stream=None) -> None:
+    _check(lib().sparsekv_gather_correct(
+        C.byref(pr), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales), _ptr(v_scales), _ptr(block_table),
+        _ptr(spec_indices), _ptr(spec_n_sel), int(spec_token), _ptr(spec_k_stage), _ptr(spec_v_stage),
+        _ptr(spec_k_scales), _ptr(spec_v_scales), _ptr(real_indices), _ptr(real_n_sel), int(real_token),
+        _ptr(k_stage), _ptr(v_stage), _ptr(k_stage_scales), _ptr(v_stage_scales), _ptr(misses),
+        _stream(stream)), "sparsekv_gather_correct")
 
 
 def kv_source(kind: int, k, v, k_scales=None, v_scales=None, block_table=None) -> KvSource:

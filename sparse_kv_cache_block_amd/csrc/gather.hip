@@ -11,26 +11,74 @@
 // be device memory or pinned host memory read over the host link; in the
 // host-major pool layout neighbouring selected blocks of a head are adjacent,
 // so runs of them form one sequential stream.
+//
+// The same kernel corrects a speculative prefetch (DualDecoder, mechanism
+// summary and Fig. 19): blocks staged for a speculative selection are moved
+// into the real selection's slots on the GPU, and only the misses are read
+// from the pool.
 #include "skv_device.h"
 #include "skv_internal.h"
 
 namespace skv {
 
+// First position of `id` in the ascending ids[0..n), or -1.
+__device__ __forceinline__ int find_sorted(const int32_t* ids, int n, int id) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ids[mid] < id) lo = mid + 1; else hi = mid;
+  }
+  return lo < n && ids[lo] == id ? lo : -1;
+}
+
+// Grid (slot m, KV head g, sequence b).  With a speculative selection, the
+// chunk comes from the speculative stage when the speculative row holds the
+// block (the reorder), else from the pool (a miss); the slot-0 workgroup of
+// each row also counts the row's misses.
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherParams p) {
   const int m = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int64_t row = (int64_t)b * p.T * p.Hkv + g;  // token 0 selection
-  if (m >= p.n_sel[row]) return;
-  const int j = p.indices[row * p.k_max + m];
-  const int64_t phys = p.block_table[(int64_t)b * p.max_blocks + j];
-  const int64_t src_off = (phys * p.stride_block + (int64_t)g * p.stride_head) * p.elem_bytes;
+  const int64_t row = ((int64_t)b * p.T + p.token) * p.Hkv + g;
+  const int n_real = p.n_sel[row];
+  const int32_t* real_ids = p.indices + row * p.k_max;
+  const int64_t srow = ((int64_t)b * p.T + p.spec_token) * p.Hkv + g;
+  const int n_spec = p.spec_indices ? min(p.spec_n_sel[srow], p.k_max) : 0;
+  const int32_t* spec_ids = p.spec_indices ? p.spec_indices + srow * p.k_max : nullptr;
+
+  if (m == 0 && p.misses) {
+    __shared__ int s_miss;
+    if (threadIdx.x == 0) s_miss = 0;
+    __syncthreads();
+    int local = 0;
+    for (int i = threadIdx.x; i < n_real; i += kThreads)
+      local += (spec_ids ? find_sorted(spec_ids, n_spec, real_ids[i]) : -1) < 0;
+    if (local) atomicAdd(&s_miss, local);
+    __syncthreads();
+    if (threadIdx.x == 0) p.misses[(int64_t)b * p.Hkv + g] = s_miss;
+  }
+  if (m >= n_real) return;
+
+  const int j = real_ids[m];
+  const int ms = spec_ids ? find_sorted(spec_ids, n_spec, j) : -1;
   const int64_t slot = ((int64_t)b * p.Hkv + g) * p.k_max + m;
   const int64_t dst_off = slot * p.chunk_bytes;
+  const char* ksrc;
+  const char* vsrc;
+  int64_t phys = 0, sslot = 0;
+  if (ms >= 0) {   // reorder: from the speculative slot
+    sslot = ((int64_t)b * p.Hkv + g) * p.k_max + ms;
+    ksrc = static_cast<const char*>(p.spec_k_stage) + sslot * p.chunk_bytes;
+    vsrc = static_cast<const char*>(p.spec_v_stage) + sslot * p.chunk_bytes;
+  } else {         // from the pool
+    phys = p.block_table[(int64_t)b * p.max_blocks + j];
+    const int64_t src_off = (phys * p.stride_block + (int64_t)g * p.stride_head) * p.elem_bytes;
+    ksrc = static_cast<const char*>(p.k_pool) + src_off;
+    vsrc = static_cast<const char*>(p.v_pool) + src_off;
+  }
   const int nvec = (int)(p.chunk_bytes / 16);
   constexpr int UR = 4;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(which ? p.v_pool : p.k_pool) + src_off);
+    const uint4* src = reinterpret_cast<const uint4*>(which ? vsrc : ksrc);
     uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(which ? p.v_stage : p.k_stage) + dst_off);
     for (int base = threadIdx.x; base < nvec; base += UR * kThreads) {
       uint4 v[UR];
@@ -47,8 +95,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherParams p) {
     }
   }
   if (p.has_scales && threadIdx.x == 0) {
-    p.k_stage_scales[slot] = p.k_scales[phys * p.Hkv + g];
-    p.v_stage_scales[slot] = p.v_scales[phys * p.Hkv + g];
+    p.k_stage_scales[slot] = ms >= 0 ? p.spec_k_scales[sslot] : p.k_scales[phys * p.Hkv + g];
+    p.v_stage_scales[slot] = ms >= 0 ? p.spec_v_scales[sslot] : p.v_scales[phys * p.Hkv + g];
   }
 }
 

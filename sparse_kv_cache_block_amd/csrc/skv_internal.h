@@ -97,6 +97,16 @@ struct GatherParams {
   int64_t chunk_bytes;      // blk * d * element size
   int elem_bytes;
   int has_scales;
+  int token;                // the selection gathered: token `token` of indices / n_sel
+  // speculative correction (null spec_indices: a plain gather)
+  const int32_t* spec_indices;
+  const int32_t* spec_n_sel;
+  int spec_token;
+  const void* spec_k_stage;
+  const void* spec_v_stage;
+  const float* spec_k_scales;
+  const float* spec_v_scales;
+  int32_t* misses;          // [B][Hkv] or null
 };
 
 // Launch shapes decided on the host; the workspace layout depends on them.

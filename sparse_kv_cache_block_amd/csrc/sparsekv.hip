@@ -335,23 +335,19 @@ skv_status enqueue_step(const skv_problem& p, const Plan& pl, const skv_step_inp
   return SKV_OK;
 }
 
-skv_status enqueue_host_layer(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
-                              const skv_step_outputs& out, void* k_stage, void* v_stage,
-                              float* k_stage_scales, float* v_stage_scales, char* ws,
-                              hipStream_t s, hipStream_t cs, hipEvent_t ev_sel, hipEvent_t ev_gather,
-                              hipEvent_t slot_free) {
-  // the copy stream waits for this layer's indices (and for the slot to be free)
-  SKV_TRY_HIP(hipEventRecord(ev_sel, s), "event record");
-  SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel, 0), "stream wait");
-  if (slot_free) SKV_TRY_HIP(hipStreamWaitEvent(cs, slot_free, 0), "stream wait");
+// Gather of token 0's selection (the fields of a speculative correction stay null).
+GatherParams gather_params(const skv_problem& p, const void* k_pool, const void* v_pool,
+                           const float* k_scales, const float* v_scales, const int32_t* block_table,
+                           const int32_t* indices, const int32_t* n_sel, void* k_stage, void* v_stage,
+                           float* k_stage_scales, float* v_stage_scales) {
   GatherParams gp{};
-  gp.k_pool = in.k_pool;
-  gp.v_pool = in.v_pool;
-  gp.k_scales = in.k_scales;
-  gp.v_scales = in.v_scales;
-  gp.block_table = in.block_table;
-  gp.indices = out.indices;
-  gp.n_sel = out.n_sel;
+  gp.k_pool = k_pool;
+  gp.v_pool = v_pool;
+  gp.k_scales = k_scales;
+  gp.v_scales = v_scales;
+  gp.block_table = block_table;
+  gp.indices = indices;
+  gp.n_sel = n_sel;
   gp.k_stage = k_stage;
   gp.v_stage = v_stage;
   gp.k_stage_scales = k_stage_scales;
@@ -366,6 +362,20 @@ skv_status enqueue_host_layer(const skv_problem& p, const Plan& pl, const skv_st
   gp.elem_bytes = elem_bytes(p.kv_dtype);
   gp.chunk_bytes = (int64_t)p.block_size * p.head_dim * gp.elem_bytes;
   gp.has_scales = p.kv_dtype == SKV_FP8_E4M3FN;
+  return gp;
+}
+
+skv_status enqueue_host_layer(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                              const skv_step_outputs& out, void* k_stage, void* v_stage,
+                              float* k_stage_scales, float* v_stage_scales, char* ws,
+                              hipStream_t s, hipStream_t cs, hipEvent_t ev_sel, hipEvent_t ev_gather,
+                              hipEvent_t slot_free) {
+  // the copy stream waits for this layer's indices (and for the slot to be free)
+  SKV_TRY_HIP(hipEventRecord(ev_sel, s), "event record");
+  SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel, 0), "stream wait");
+  if (slot_free) SKV_TRY_HIP(hipStreamWaitEvent(cs, slot_free, 0), "stream wait");
+  GatherParams gp = gather_params(p, in.k_pool, in.v_pool, in.k_scales, in.v_scales, in.block_table,
+                                  out.indices, out.n_sel, k_stage, v_stage, k_stage_scales, v_stage_scales);
   SKV_TRY_HIP(launch_gather(gp, cs), "gather launch");
   SKV_TRY_HIP(hipEventRecord(ev_gather, cs), "event record");
   SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather, 0), "stream wait");
@@ -500,29 +510,55 @@ skv_status sparsekv_gather(const skv_problem* pr, const void* k_pool, const void
   const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
   if (fp8 && (!k_scales || !v_scales || !k_stage_scales || !v_stage_scales))
     return fail(SKV_E_NULL, "gather: fp8 needs pool and stage scales");
-  GatherParams gp{};
-  gp.k_pool = k_pool;
-  gp.v_pool = v_pool;
-  gp.k_scales = k_scales;
-  gp.v_scales = v_scales;
-  gp.block_table = block_table;
-  gp.indices = indices;
-  gp.n_sel = n_sel;
-  gp.k_stage = k_stage;
-  gp.v_stage = v_stage;
-  gp.k_stage_scales = k_stage_scales;
-  gp.v_stage_scales = v_stage_scales;
-  gp.B = p.batch;
-  gp.T = p.n_q_tokens;
-  gp.Hkv = p.n_kv_heads;
-  gp.max_blocks = p.max_blocks_per_seq;
-  gp.k_max = p.k_max;
-  gp.stride_block = p.pool_stride_block;
-  gp.stride_head = p.pool_stride_head;
-  gp.elem_bytes = elem_bytes(p.kv_dtype);
-  gp.chunk_bytes = (int64_t)p.block_size * p.head_dim * gp.elem_bytes;
-  gp.has_scales = fp8;
+  GatherParams gp = gather_params(p, k_pool, v_pool, k_scales, v_scales, block_table, indices, n_sel,
+                                  k_stage, v_stage, k_stage_scales, v_stage_scales);
   SKV_TRY_HIP(launch_gather(gp, as_stream(stream)), "gather launch");
+  return SKV_OK;
+}
+
+skv_status sparsekv_gather_correct(const skv_problem* pr, const void* k_pool, const void* v_pool,
+                                   const float* k_scales, const float* v_scales,
+                                   const int32_t* block_table, const int32_t* spec_indices,
+                                   const int32_t* spec_n_sel, int32_t spec_token,
+                                   const void* spec_k_stage, const void* spec_v_stage,
+                                   const float* spec_k_scales, const float* spec_v_scales,
+                                   const int32_t* real_indices, const int32_t* real_n_sel,
+                                   int32_t real_token, void* k_stage, void* v_stage,
+                                   float* k_stage_scales, float* v_stage_scales, int32_t* misses,
+                                   void* stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  if (!k_pool || !v_pool || !block_table || !spec_indices || !spec_n_sel || !spec_k_stage ||
+      !spec_v_stage || !real_indices || !real_n_sel || !k_stage || !v_stage)
+    return fail(SKV_E_NULL, "gather_correct: NULL argument");
+  if (spec_token < 0 || spec_token >= p.n_q_tokens || real_token < 0 || real_token >= p.n_q_tokens)
+    return fail(SKV_E_SHAPE, "gather_correct: tokens %d, %d not in [0, %d)", spec_token, real_token,
+                p.n_q_tokens);
+  const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
+  if (fp8 && (!k_scales || !v_scales || !k_stage_scales || !v_stage_scales || !spec_k_scales ||
+              !spec_v_scales))
+    return fail(SKV_E_NULL, "gather_correct: fp8 needs pool and stage scales");
+  const size_t stage_bytes = (size_t)p.batch * p.n_kv_heads * p.k_max * p.block_size * p.head_dim *
+                             elem_bytes(p.kv_dtype);
+  auto overlaps = [&](const void* a, const void* b) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + stage_bytes && y < x + stage_bytes;
+  };
+  if (overlaps(k_stage, spec_k_stage) || overlaps(v_stage, spec_v_stage))
+    return fail(SKV_E_SHAPE, "gather_correct: the speculative and the output stages overlap");
+  GatherParams gp = gather_params(p, k_pool, v_pool, k_scales, v_scales, block_table, real_indices,
+                                  real_n_sel, k_stage, v_stage, k_stage_scales, v_stage_scales);
+  gp.token = real_token;
+  gp.spec_indices = spec_indices;
+  gp.spec_n_sel = spec_n_sel;
+  gp.spec_token = spec_token;
+  gp.spec_k_stage = spec_k_stage;
+  gp.spec_v_stage = spec_v_stage;
+  gp.spec_k_scales = spec_k_scales;
+  gp.spec_v_scales = spec_v_scales;
+  gp.misses = misses;
+  SKV_TRY_HIP(launch_gather(gp, as_stream(stream)), "gather_correct launch");
   return SKV_OK;
 }
 
@@ -612,28 +648,10 @@ skv_status sparsekv_decode_layers(const skv_problem* pr, int32_t n_layers, const
     const int slot = l & 1;
     SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel[l], 0), "stream wait");
     if (l >= 2) SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_attn[l - 2], 0), "stream wait");
-    GatherParams gp{};
-    gp.k_pool = in[l].k_pool;
-    gp.v_pool = in[l].v_pool;
-    gp.k_scales = in[l].k_scales;
-    gp.v_scales = in[l].v_scales;
-    gp.block_table = in[l].block_table;
-    gp.indices = out[l].indices;
-    gp.n_sel = out[l].n_sel;
-    gp.k_stage = k_stage[slot];
-    gp.v_stage = v_stage[slot];
-    gp.k_stage_scales = k_stage_scales ? k_stage_scales[slot] : nullptr;
-    gp.v_stage_scales = v_stage_scales ? v_stage_scales[slot] : nullptr;
-    gp.B = p.batch;
-    gp.T = p.n_q_tokens;
-    gp.Hkv = p.n_kv_heads;
-    gp.max_blocks = p.max_blocks_per_seq;
-    gp.k_max = p.k_max;
-    gp.stride_block = p.pool_stride_block;
-    gp.stride_head = p.pool_stride_head;
-    gp.elem_bytes = elem_bytes(p.kv_dtype);
-    gp.chunk_bytes = (int64_t)p.block_size * p.head_dim * gp.elem_bytes;
-    gp.has_scales = p.kv_dtype == SKV_FP8_E4M3FN;
+    GatherParams gp = gather_params(p, in[l].k_pool, in[l].v_pool, in[l].k_scales, in[l].v_scales,
+                                    in[l].block_table, out[l].indices, out[l].n_sel, k_stage[slot],
+                                    v_stage[slot], k_stage_scales ? k_stage_scales[slot] : nullptr,
+                                    v_stage_scales ? v_stage_scales[slot] : nullptr);
     SKV_TRY_HIP(launch_gather(gp, cs), "gather launch");
     SKV_TRY_HIP(hipEventRecord(ev_gather[l], cs), "event record");
     SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather[l], 0), "stream wait");

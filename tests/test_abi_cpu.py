@@ -127,3 +127,23 @@ def test_fp8_needs_scales(lib):
     st = lib.sparsekv_attend(C.byref(pr), 0x1000, C.byref(src), 0x1000, 0x1000, C.byref(src), 0x1000,
                              0x1000, None, 0x1000, n, None)
     assert st == B.SKV_E_NULL
+
+
+def _gather_correct(lib, pr, spec_token=0, real_token=0, spec_indices=0x1000, spec_stage=0x200000,
+                    out_stage=0x100000000, scales=None):
+    d = 0x1000
+    return lib.sparsekv_gather_correct(C.byref(pr), d, d, scales, scales, d, spec_indices, d, spec_token,
+                                       spec_stage, spec_stage, scales, scales, d, d, real_token,
+                                       out_stage, out_stage, scales, scales, None, None)
+
+
+def test_gather_correct_validation(lib):
+    pr = _good_problem(T=2)
+    # every check runs on the host, before any launch
+    assert _gather_correct(lib, pr, spec_indices=None) == B.SKV_E_NULL
+    assert _gather_correct(lib, pr, spec_token=2) == B.SKV_E_SHAPE
+    assert _gather_correct(lib, pr, real_token=-1) == B.SKV_E_SHAPE
+    # stage bytes: B * Hkv * k_max * blk * d * 2 = 2*2*8*32*128*2 = 256 KiB: overlapping ranges
+    assert _gather_correct(lib, pr, spec_stage=0x200000, out_stage=0x200000 + 0x1000) == B.SKV_E_SHAPE
+    assert _gather_correct(lib, _good_problem(T=2, kv_dtype="fp8")) == B.SKV_E_NULL
+    assert "gather_correct" in B.sparsekv_last_error()

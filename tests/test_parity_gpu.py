@@ -285,6 +285,67 @@ def test_gather_and_attend_entry_points():
         assert (lse2 - st.lse).abs().max().item() <= 2e-5
 
 
+@pytest.mark.parametrize("wl", [configs.DUAL.scaled(batch=2, context=8192, top_k=30),
+                                configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3)])
+def test_speculative_gather_correction(wl):
+    # stage the speculative token's selection, then correct it to the real
+    # token's: the result must be the real selection's gather, byte for byte
+    announce(f"sparsekv_gather_correct ({wl.name}, pool={wl.pool})")
+    inp, st = run_step(wl)
+    dev, pr = st.inp, st.pr
+    Bn, Hkv, km = wl.batch, wl.n_kv_heads, pr.k_max
+    shape = (Bn, Hkv, km, wl.block_size, wl.head_dim)
+    fp8 = dev.k_scales is not None
+
+    def stage():
+        k = torch.zeros(shape, dtype=dev.k_pool.dtype, device="cuda")
+        v = torch.zeros(shape, dtype=dev.v_pool.dtype, device="cuda")
+        ks = torch.zeros((Bn, Hkv, km), dtype=torch.float32, device="cuda") if fp8 else None
+        vs = torch.zeros((Bn, Hkv, km), dtype=torch.float32, device="cuda") if fp8 else None
+        return k, v, ks, vs
+
+    pools = (dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales, dev.block_table)
+    none_n = torch.zeros_like(st.n_sel)
+    spare, spec, out, ref = stage(), stage(), stage(), stage()
+    miss_spec = torch.full((Bn, Hkv), -1, dtype=torch.int32, device="cuda")
+    miss = torch.full((Bn, Hkv), -1, dtype=torch.int32, device="cuda")
+    # an empty speculative row: every block of token 1 is a miss
+    B.sparsekv_gather_correct(pr, *pools, st.indices, none_n, 0, spare[0], spare[1], spare[2], spare[3],
+                              st.indices, st.n_sel, 1, *spec, misses=miss_spec)
+    # the correction from token 1's stage to token 0's selection
+    B.sparsekv_gather_correct(pr, *pools, st.indices, st.n_sel, 1, *spec, st.indices, st.n_sel, 0, *out,
+                              misses=miss)
+    B.sparsekv_gather(pr, *pools, st.indices, st.n_sel, *ref)
+    torch.cuda.synchronize()
+
+    from sparse_kv_cache_block_amd.inputs import raw_bytes
+    idx, nsel = _np(st.indices), _np(st.n_sel)
+    h = HostArrays(inp)
+    oks, ovs, okss, ovss = O.gather(oracle_problem(inp, k_max=km), *h.pools(), h.block_table, idx, nsel)
+    for b in range(Bn):
+        for g in range(Hkv):
+            n0, n1 = int(nsel[b, 0, g]), int(nsel[b, 1, g])
+            common = len(set(idx[b, 0, g, :n0].tolist()) & set(idx[b, 1, g, :n1].tolist()))
+            assert int(miss[b, g]) == n0 - common
+            assert int(miss_spec[b, g]) == n1
+            for a, r in ((out[0], ref[0]), (out[1], ref[1])):
+                assert np.array_equal(raw_bytes(a)[b, g, :n0].view(np.uint8), raw_bytes(r)[b, g, :n0].view(np.uint8))
+            assert np.array_equal(raw_bytes(out[0])[b, g, :n0].view(np.uint8), oks[b, g, :n0].view(np.uint8))
+            assert np.array_equal(raw_bytes(out[1])[b, g, :n0].view(np.uint8), ovs[b, g, :n0].view(np.uint8))
+            if fp8:
+                assert np.array_equal(_np(out[2])[b, g, :n0], okss[b, g, :n0])
+                assert np.array_equal(_np(out[3])[b, g, :n0], ovss[b, g, :n0])
+    # identical selections: nothing is missed, the stage is moved as it is
+    B.sparsekv_gather_correct(pr, *pools, st.indices, st.n_sel, 0, *ref, st.indices, st.n_sel, 0, *spare,
+                              misses=miss)
+    torch.cuda.synchronize()
+    assert int(miss.abs().sum()) == 0
+    for b in range(Bn):
+        for g in range(Hkv):
+            n0 = int(nsel[b, 0, g])
+            assert torch.equal(spare[0][b, g, :n0], ref[0][b, g, :n0])
+
+
 def test_host_layer_pipeline_matches_single_steps():
     wl = configs.HOST.scaled(batch=2, context=8192)
     announce("sparsekv_decode_layers (ping-pong, 4 layers) vs single steps")
