@@ -113,6 +113,62 @@ def h2d_ceiling_gbps(mib: int = 64, reps: int = 20) -> float:
     return n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+def gather_correct_probe(reps: int) -> int:
+    """Host-pool workload with a speculative second query token (real + N(0, 0.3)):
+    the full gather of the real token's selection against the correction of a
+    stage already holding the speculative token's selection."""
+    import numpy as np
+    import torch
+
+    from sparse_kv_cache_block_amd import binding as B
+    from sparse_kv_cache_block_amd import configs
+    from sparse_kv_cache_block_amd.inputs import make_inputs
+    from sparse_kv_cache_block_amd.step import DecodeStep, to_device_for
+
+    wl = configs.HOST.scaled(n_q_tokens=2, spec_noise=0.3)
+    torch.cuda.set_device(0)
+    st = DecodeStep(to_device_for(make_inputs(wl, device="cuda", instance=0)))
+    st.run()
+    torch.cuda.synchronize()
+    d, pr = st.inp, st.pr
+    shape = (wl.batch, wl.n_kv_heads, pr.k_max, wl.block_size, wl.head_dim)
+    stages = [(torch.empty(shape, dtype=d.k_pool.dtype, device="cuda"),
+               torch.empty(shape, dtype=d.v_pool.dtype, device="cuda")) for _ in range(3)]
+    pools = (d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
+    misses = torch.empty((wl.batch, wl.n_kv_heads), dtype=torch.int32, device="cuda")
+    spec, out, full = stages
+    none_n = torch.zeros_like(st.n_sel)
+    B.sparsekv_gather_correct(pr, *pools, st.indices, none_n, 0, *full, None, None, st.indices, st.n_sel, 1,
+                              *spec)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn) -> float:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    t_full = timed(lambda: B.sparsekv_gather(pr, *pools, st.indices, st.n_sel, *full))
+    t_corr = timed(lambda: B.sparsekv_gather_correct(pr, *pools, st.indices, st.n_sel, 1, *spec, None, None,
+                                                     st.indices, st.n_sel, 0, *out, misses=misses))
+    chunk = 2 * wl.block_size * wl.head_dim * 2
+    n_real = int(st.n_sel[:, 0].sum())
+    n_miss = int(misses.sum())
+    print(json.dumps({
+        "probe": "gather_correct", "workload": "host, 2 query tokens, speculative = real + N(0, 0.3)",
+        "reps": reps, "full_gather_us": round(t_full, 1), "correction_us": round(t_corr, 1),
+        "speedup": round(t_full / t_corr, 2), "selected_chunks": n_real, "misses": n_miss,
+        "miss_fraction": round(n_miss / max(1, n_real), 4),
+        "host_link_bytes_full": n_real * chunk, "host_link_bytes_correction": n_miss * chunk,
+        "overlap_mean": round(float(np.mean(st.overlap.cpu().numpy())), 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,9 +181,13 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0 disables it)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--gather-correct", action="store_true",
+                    help="only compare the full host gather with the speculative correction and exit")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe, max(1, args.steps))
+    if args.gather_correct:
+        return gather_correct_probe(max(1, min(args.steps, 50)))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
