@@ -52,7 +52,8 @@ def attention_bytes(wl, seq_lens, nsel_real) -> int:
 
 KERNEL_SOURCES = {
     "pair_step_kernel": ("step.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
-    "attend_kernel": ("attend.hip", "attend_dev.h", "skv_device.h", "skv_internal.h"),
+    "attend_kernel": ("attend.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
+    "attend_cobatched_kernel": ("attend.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
 }
 
 
@@ -169,6 +170,95 @@ def gather_correct_probe(reps: int) -> int:
     return 0
 
 
+def cobatched_probe(reps: int, instances: int) -> int:
+    """Dual workload: both query tokens attended by one co-batched launch over
+    the union of their selections, against one attention launch per token."""
+    import torch
+
+    from sparse_kv_cache_block_amd import binding as B
+    from sparse_kv_cache_block_amd import configs
+    from sparse_kv_cache_block_amd.configs import ELEM_BYTES
+    from sparse_kv_cache_block_amd.inputs import make_inputs
+    from sparse_kv_cache_block_amd.step import DecodeStep
+
+    wl = configs.DUAL
+    torch.cuda.set_device(0)
+    runs = []
+    for i in range(instances):
+        st = DecodeStep(make_inputs(wl, device="cuda", instance=i))
+        st.run()
+        d = st.inp
+        src = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
+        Bn, Hq, D = d.q.shape[0], d.q.shape[2], d.q.shape[3]
+        out2 = torch.empty((Bn, 2, Hq, D), dtype=torch.float32, device="cuda")
+        lse2 = torch.empty((Bn, 2, Hq), dtype=torch.float32, device="cuda")
+        outs = [torch.empty((Bn, Hq, D), dtype=torch.float32, device="cuda") for _ in range(2)]
+        lses = [torch.empty((Bn, Hq), dtype=torch.float32, device="cuda") for _ in range(2)]
+        runs.append((st, src, out2, lse2, outs, lses))
+    torch.cuda.synchronize()
+
+    def two_launches(k):
+        st, src, _, _, outs, lses = runs[k % len(runs)]
+        d = st.inp
+        for t in range(2):
+            B.sparsekv_attend(st.pr, d.q[:, t:], src, st.indices[:, t:], st.n_sel[:, t:], src, d.seq_lens,
+                              outs[t], lses[t], st.ws)
+
+    def cobatched(k):
+        st, src, out2, lse2, _, _ = runs[k % len(runs)]
+        d = st.inp
+        B.sparsekv_attend_cobatched(st.pr, d.q, src, st.indices, st.n_sel, src, d.seq_lens, out2, lse2, st.ws)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn) -> float:
+        for k in range(5):
+            fn(k)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for k in range(reps):
+            fn(k)
+        ev[1].record()
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    # interleave the two so that both see the same clocks
+    t_two, t_cob = [], []
+    for _ in range(3):
+        t_two.append(timed(two_launches))
+        t_cob.append(timed(cobatched))
+    t_two, t_cob = statistics.median(t_two), statistics.median(t_cob)
+    # the two outputs agree (same values up to fp32 summation order)
+    st, _, out2, lse2, outs, lses = runs[0]
+    two_launches(0)
+    cobatched(0)
+    torch.cuda.synchronize()
+    diff = max((out2[:, t] - outs[t]).abs().max().item() for t in range(2))
+
+    chunk = 2 * wl.block_size * wl.head_dim * ELEM_BYTES[wl.kv_dtype] + 8
+    idx, nsel = st.indices.cpu().numpy(), st.n_sel.cpu().numpy()
+    union = sel = 0
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            a0 = set(idx[b, 0, g, :nsel[b, 0, g]].tolist())
+            a1 = set(idx[b, 1, g, :nsel[b, 1, g]].tolist())
+            union += len(a0 | a1)
+            sel += len(a0) + len(a1)
+    lens = st.inp.seq_lens.cpu().numpy()
+    win = sum(wl.n_kv_heads * min(wl.window, int(L)) * 2 * wl.head_dim * ELEM_BYTES[wl.kv_dtype] for L in lens)
+    qo = wl.batch * 2 * wl.n_q_heads * (wl.head_dim * 2 + (wl.head_dim + 1) * 4)
+    cob_bytes = union * chunk + win + qo
+    print(json.dumps({
+        "probe": "cobatched_attention", "workload": "dual (B4, L262144, Hq64/Hkv8, blk64, k128, W1024, fp8)",
+        "reps": reps, "instances": instances,
+        "two_launches_us": round(t_two, 2), "cobatched_us": round(t_cob, 2),
+        "saving": round(1 - t_cob / t_two, 3), "max_abs_diff": diff,
+        "selected_blocks_two_tokens": sel, "union_blocks": union,
+        "cobatched_bytes": cob_bytes, "cobatched_gbps": round(cob_bytes / (t_cob * 1e-6) / 1e9, 1),
+        "two_launch_bytes": sel * chunk + 2 * win + qo}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,11 +273,15 @@ def main() -> int:
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--gather-correct", action="store_true",
                     help="only compare the full host gather with the speculative correction and exit")
+    ap.add_argument("--cobatched", action="store_true",
+                    help="only compare co-batched two-token attention with one launch per token and exit")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe, max(1, args.steps))
     if args.gather_correct:
         return gather_correct_probe(max(1, min(args.steps, 50)))
+    if args.cobatched:
+        return cobatched_probe(max(1, args.steps), max(1, args.instances))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -38,7 +38,8 @@
  *   n_sel      [B][T][Hkv] int32 = min(k_b, #candidates)
  *   stage      [B][Hkv][k_max][blk][d] kv_dtype; stage scales [B][Hkv][k_max]
  *   window buf [B][Hkv][W][d] kv_dtype: row r holds position ws_b + r
- *   out        [B][Hq][d] fp32 (real token), lse [B][Hq] fp32 (natural log)
+ *   out        [B][Hq][d] fp32 (real token), lse [B][Hq] fp32 (natural log);
+ *              co-batched attention: [B][T][Hq][d] and [B][T][Hq]
  *   overlap    [B][Hkv] fp32 = |I_real & I_spec| / |I_real| (T == 2)
  *
  * Ownership and execution: the caller owns every buffer (device memory, or
@@ -239,6 +240,27 @@ skv_status sparsekv_attend(const skv_problem *pr, const void *q, const skv_kv_so
                            const skv_kv_source *window, const int32_t *seq_lens,
                            float *out, float *lse, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * Co-batched attention of both query tokens (DualDecoder review, Fig. 18:
+ * the real and the speculative token attended in one launch instead of
+ * two).  For t in {0, 1}, out[b,t,h,:] and lse[b,t,h] are exactly what
+ * sparsekv_attend computes for token t alone -- token t's query over token
+ * t's own selection (indices / n_sel rows of token t) plus the window
+ * [ws_b, L_b) -- up to fp32 rounding order.  Each block of the union of the
+ * two selections is read once per (sequence, KV head); a block that only one
+ * token selected is masked for the other.  out is [B][T][Hq][d] fp32, lse
+ * [B][T][Hq] (may be NULL).  T == 2 needs a device pool and a PAGED sparse
+ * source (the union is read through the block table); SKV_E_UNSUPPORTED
+ * otherwise, and for k_max large enough that the split merge would not fit
+ * in a workgroup's LDS.  T == 1 is sparsekv_attend.  The workspace is the
+ * one sparsekv_workspace_size gives for the problem.
+ */
+skv_status sparsekv_attend_cobatched(const skv_problem *pr, const void *q,
+                                     const skv_kv_source *sparse, const int32_t *indices,
+                                     const int32_t *n_sel, const skv_kv_source *window,
+                                     const int32_t *seq_lens, float *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Full decode step.  Device pool: scoring with in-kernel top-k, then

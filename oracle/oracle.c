@@ -39,6 +39,9 @@
  *             o = sum_i e^{lse_i - M} o_i / sum_i e^{lse_i - M},
  *             lse = M + ln sum_i e^{lse_i - M}.
  *           An empty part has lse = -inf and weight 0.
+ *           attend_tokens applies the same to every query token t (its own
+ *           query and its own selection): the co-batched two-token attention
+ *           of DualDecoder Fig. 18 computes exactly these values.
  *  overlap  DualDecoder core claim / Fig. 16: retrieval-index prediction
  *           accuracy = |I_real & I_spec| / |I_real| per (sequence, KV head).
  *
@@ -228,9 +231,9 @@ void orc_gather(const orc_problem *pr, const void *k_pool, const void *v_pool,
  * positions: m = max z, l = sum e^{z-m}, o = sum e^{z-m} v / l, lse = m + ln l.
  * An empty list gives lse = -inf and o = 0.
  */
-void orc_partial(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
-                 const float *k_scales, const float *v_scales, const int32_t *block_table,
-                 int b, int h, const int64_t *pos, int n_pos, double *o, double *lse) {
+static void partial_tok(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
+                        const float *k_scales, const float *v_scales, const int32_t *block_table,
+                        int b, int t, int h, const int64_t *pos, int n_pos, double *o, double *lse) {
     const int G = pr->Hq / pr->Hkv;
     const int g = h / G;
     const double inv_sqrt_d = 1.0 / sqrt((double)pr->d);
@@ -241,7 +244,7 @@ void orc_partial(const orc_problem *pr, const void *q, const void *k_pool, const
     for (int n = 0; n < n_pos; ++n) {
         double dot = 0.0;
         for (int i = 0; i < pr->d; ++i) {
-            double qv = load(q, pr->q_dtype, (((int64_t)b * pr->T + 0) * pr->Hq + h) * pr->d + i);
+            double qv = load(q, pr->q_dtype, (((int64_t)b * pr->T + t) * pr->Hq + h) * pr->d + i);
             dot += qv * kv_at(pr, k_pool, k_scales, block_table, b, g, pos[n], i);
         }
         z[n] = dot * inv_sqrt_d;
@@ -257,6 +260,12 @@ void orc_partial(const orc_problem *pr, const void *q, const void *k_pool, const
     for (int i = 0; i < pr->d; ++i) o[i] /= l;
     *lse = m + log(l);
     free(z);
+}
+
+void orc_partial(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
+                 const float *k_scales, const float *v_scales, const int32_t *block_table,
+                 int b, int h, const int64_t *pos, int n_pos, double *o, double *lse) {
+    partial_tok(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, 0, h, pos, n_pos, o, lse);
 }
 
 void orc_merge(int n_parts, int d, const double *o_parts, const double *lse_parts,
@@ -296,6 +305,40 @@ static int window_positions(const orc_problem *pr, int L, int64_t *pos) {
     return cnt;
 }
 
+/* Attention of query token t of (b, g) over token t's own selection plus the
+ * window: rows h of the group go to out_rows + (h - gG) * d, lse_rows[h - gG]
+ * (and the two parts to part_o / part_lse when given). */
+static void attend_pair(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
+                        const float *k_scales, const float *v_scales, const int32_t *block_table,
+                        const int32_t *seq_lens, const int32_t *indices, const int32_t *n_sel,
+                        int b, int t, int g, double *out_rows, double *lse_rows, double *part_o,
+                        double *part_lse) {
+    const int G = pr->Hq / pr->Hkv;
+    int L = seq_lens[b];
+    const int32_t *idx = indices + (((int64_t)b * pr->T + t) * pr->Hkv + g) * pr->k_max;
+    int n = n_sel[((int64_t)b * pr->T + t) * pr->Hkv + g];
+    int64_t *sp = (int64_t *)malloc(sizeof(int64_t) * ((int64_t)n * pr->blk + 1));
+    int64_t *wp = (int64_t *)malloc(sizeof(int64_t) * ((int64_t)pr->window + 1));
+    int ns = sparse_positions(pr, L, idx, n, sp);
+    int nw = window_positions(pr, L, wp);
+    double *po = (double *)malloc(sizeof(double) * 2 * pr->d);
+    double pl[2];
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+        partial_tok(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, t, h, sp, ns, po, &pl[0]);
+        partial_tok(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, t, h, wp, nw, po + pr->d, &pl[1]);
+        const int r = h - g * G;
+        if (part_o) {
+            memcpy(part_o + (int64_t)r * 2 * pr->d, po, sizeof(double) * 2 * pr->d);
+            part_lse[r * 2 + 0] = pl[0];
+            part_lse[r * 2 + 1] = pl[1];
+        }
+        orc_merge(2, pr->d, po, pl, out_rows + (int64_t)r * pr->d, lse_rows + r);
+    }
+    free(po);
+    free(sp);
+    free(wp);
+}
+
 void orc_attend(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
                 const float *k_scales, const float *v_scales, const int32_t *block_table,
                 const int32_t *seq_lens, const int32_t *indices, const int32_t *n_sel,
@@ -304,30 +347,29 @@ void orc_attend(const orc_problem *pr, const void *q, const void *k_pool, const 
 #pragma omp parallel for collapse(2) schedule(dynamic)
     for (int b = 0; b < pr->B; ++b)
         for (int g = 0; g < pr->Hkv; ++g) {
-            int L = seq_lens[b];
-            const int32_t *idx = indices + (((int64_t)b * pr->T) * pr->Hkv + g) * pr->k_max;
-            int n = n_sel[((int64_t)b * pr->T) * pr->Hkv + g];
-            int64_t *sp = (int64_t *)malloc(sizeof(int64_t) * ((int64_t)n * pr->blk + 1));
-            int64_t *wp = (int64_t *)malloc(sizeof(int64_t) * ((int64_t)pr->window + 1));
-            int ns = sparse_positions(pr, L, idx, n, sp);
-            int nw = window_positions(pr, L, wp);
-            double *po = (double *)malloc(sizeof(double) * 2 * pr->d);
-            double pl[2];
-            for (int h = g * G; h < (g + 1) * G; ++h) {
-                orc_partial(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, h, sp, ns, po, &pl[0]);
-                orc_partial(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, h, wp, nw, po + pr->d, &pl[1]);
-                int64_t bh = (int64_t)b * pr->Hq + h;
-                if (part_o) {
-                    memcpy(part_o + bh * 2 * pr->d, po, sizeof(double) * 2 * pr->d);
-                    part_lse[bh * 2 + 0] = pl[0];
-                    part_lse[bh * 2 + 1] = pl[1];
-                }
-                orc_merge(2, pr->d, po, pl, out + bh * pr->d, lse + bh);
-            }
-            free(po);
-            free(sp);
-            free(wp);
+            int64_t bh = (int64_t)b * pr->Hq + (int64_t)g * G;
+            attend_pair(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, indices, n_sel,
+                        b, 0, g, out + bh * pr->d, lse + bh, part_o ? part_o + bh * 2 * pr->d : NULL,
+                        part_lse ? part_lse + bh * 2 : NULL);
         }
+}
+
+/* DualDecoder Fig. 18 (the real and the speculative token attended together):
+ * every query token t attends its own selection plus the window, exactly as
+ * orc_attend does for token 0.  out [B][T][Hq][d], lse [B][T][Hq]. */
+void orc_attend_tokens(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
+                       const float *k_scales, const float *v_scales, const int32_t *block_table,
+                       const int32_t *seq_lens, const int32_t *indices, const int32_t *n_sel,
+                       double *out, double *lse) {
+    const int G = pr->Hq / pr->Hkv;
+#pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int b = 0; b < pr->B; ++b)
+        for (int t = 0; t < pr->T; ++t)
+            for (int g = 0; g < pr->Hkv; ++g) {
+                int64_t row = ((int64_t)b * pr->T + t) * pr->Hq + (int64_t)g * G;
+                attend_pair(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, indices,
+                            n_sel, b, t, g, out + row * pr->d, lse + row, NULL, NULL);
+            }
 }
 
 /* dense attention over every position [0, L) (reference for k = all) */
@@ -341,7 +383,7 @@ void orc_dense(const orc_problem *pr, const void *q, const void *k_pool, const v
             int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (L + 1));
             for (int p = 0; p < L; ++p) pos[p] = p;
             int64_t bh = (int64_t)b * pr->Hq + h;
-            orc_partial(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, h, pos, L,
+            partial_tok(pr, q, k_pool, v_pool, k_scales, v_scales, block_table, b, 0, h, pos, L,
                         out + bh * pr->d, lse + bh);
             free(pos);
         }

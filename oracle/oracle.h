@@ -43,6 +43,11 @@ void orc_attend(const orc_problem *pr, const void *q, const void *k_pool, const 
                 const float *k_scales, const float *v_scales, const int32_t *block_table,
                 const int32_t *seq_lens, const int32_t *indices, const int32_t *n_sel,
                 double *out, double *lse, double *part_o, double *part_lse);
+/* every query token over its own selection: out [B][T][Hq][d], lse [B][T][Hq] */
+void orc_attend_tokens(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
+                       const float *k_scales, const float *v_scales, const int32_t *block_table,
+                       const int32_t *seq_lens, const int32_t *indices, const int32_t *n_sel,
+                       double *out, double *lse);
 void orc_dense(const orc_problem *pr, const void *q, const void *k_pool, const void *v_pool,
                const float *k_scales, const float *v_scales, const int32_t *block_table,
                const int32_t *seq_lens, double *out, double *lse);

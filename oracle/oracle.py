@@ -157,6 +157,16 @@ def attend(pr: Problem, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_
     return out, lse
 
 
+def attend_tokens(pr: Problem, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, idx, nsel):
+    """Every query token over its own selection plus the window: out [B][T][Hq][d], lse [B][T][Hq]."""
+    out = np.empty((pr.B, pr.T, pr.Hq, pr.d), dtype=np.float64)
+    lse = np.empty((pr.B, pr.T, pr.Hq), dtype=np.float64)
+    bt, sl, idx, nsel = _i32(block_table), _i32(seq_lens), _i32(idx), _i32(nsel)
+    lib().orc_attend_tokens(C.byref(pr), _p(q), _p(k_pool), _p(v_pool), _p(k_scales), _p(v_scales),
+                            _p(bt), _p(sl), _p(idx), _p(nsel), _p(out), _p(lse))
+    return out, lse
+
+
 def dense(pr: Problem, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens):
     out = np.empty((pr.B, pr.Hq, pr.d), dtype=np.float64)
     lse = np.empty((pr.B, pr.Hq), dtype=np.float64)

@@ -25,7 +25,8 @@ DTYPE_CODE = {"fp32": SKV_F32, "bf16": SKV_BF16, "fp8": SKV_FP8_E4M3FN}
 EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_workspace_size", "sparsekv_workspace_init", "sparsekv_score",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
-            "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct")
+            "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
+            "sparsekv_attend_cobatched")
 
 
 class SkvError(RuntimeError):
@@ -88,6 +89,8 @@ def lib() -> C.CDLL:
             "sparsekv_decode_step_launches": (C.c_int, [P, C.POINTER(C.c_int32)]),
             "sparsekv_attend": (C.c_int, [P, vp, C.POINTER(KvSource), vp, vp, C.POINTER(KvSource),
                                           vp, vp, vp, vp, sz, vp]),
+            "sparsekv_attend_cobatched": (C.c_int, [P, vp, C.POINTER(KvSource), vp, vp,
+                                                    C.POINTER(KvSource), vp, vp, vp, vp, sz, vp]),
             "sparsekv_decode_step": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
                                                vp, vp, vp, vp, vp, sz, vp, vp]),
             "sparsekv_decode_layers": (C.c_int, [P, C.c_int32, C.POINTER(StepInputs),
@@ -199,6 +202,15 @@ def sparsekv_attend(pr: Problem, q, sparse: KvSource, indices, n_sel, window: Op
                                  _ptr(out), _ptr(lse), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "sparsekv_attend")
+
+
+def sparsekv_attend_cobatched(pr: Problem, q, sparse: KvSource, indices, n_sel, window: Optional[KvSource],
+                              seq_lens, out, lse, workspace: torch.Tensor, stream=None) -> None:
+    _check(lib().sparsekv_attend_cobatched(
+        C.byref(pr), _ptr(q), C.byref(sparse), _ptr(indices), _ptr(n_sel),
+        C.byref(window) if window is not None else None, _ptr(seq_lens), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "sparsekv_attend_cobatched")
 
 
 def step_inputs(q, landmarks, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, k_per_seq,

@@ -26,7 +26,14 @@
 // scale multiplies the logits and the V scale multiplies P.  The next item's
 // K/V loads are issued before the current item's softmax and P V, so each
 // wave keeps one item in flight while it computes.  Online softmax runs in
-// the log2 domain in fp32.  The waves' partials are combined in LDS; each
+// the log2 domain in fp32.
+//
+// Co-batched attention of two query tokens (DualDecoder review, Fig. 18: the
+// real and the speculative token attended in one launch): the 16 columns hold
+// the 2G (token, head) pairs, the low half of P takes a second MFMA, and the
+// sparse items are the union of the two tokens' selections; an item that one
+// token did not select is masked in that token's columns, so each token's
+// result is its own attention over its own selection plus the window.  The waves' partials are combined in LDS; each
 // workgroup publishes (max, sum, unnormalised O) per head, and the last
 // workgroup of the (sequence, KV head) merges all of them into the fp32
 // output and lse.
@@ -66,7 +73,7 @@ struct AttnCfg {
 struct ItemDesc {
   int row;        // physical block (paged source), staging slot, or first token row (window buffer)
   int pos0;       // sequence position of the item's row 0; bit 31 marks a window item
-  int sub;        // slice of the block
+  int sub;        // slice of the block (bits 0-7); bits 8-9: query tokens that skip the item
 };
 
 // Slice `sub` of the m-th selected block of (b, g), block id j.  A paged
@@ -142,8 +149,8 @@ __device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws)
 // path has the same count of loads in flight); post() runs after pre (both
 // hooks run in every thread).  Leaves each wave's unnormalised O rows,
 // running max and sum in its LDS combine region.
-template <int KV, int D, int BLK, int NW, class EarlyDescFn, class LateDescFn, class EarlyFn, class PreFn,
-          class PostFn>
+template <int KV, int D, int BLK, int NW, int NTOK = 1, class EarlyDescFn, class LateDescFn, class EarlyFn,
+          class PreFn, class PostFn>
 __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, int b, int g, int first,
                                              int count, EarlyDescFn desc_early, LateDescFn desc_late,
                                              EarlyFn early, PreFn pre, PostFn post) {
@@ -155,13 +162,20 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   const int L = p.seq_lens[b];
   const int ws = L - p.window > 0 ? L - p.window : 0;
 
-  // ---- query operand: column n holds head n (and head n-G for the low half)
-  const int ncols = KV == KV_F32 ? G : 2 * G;
-  const int hq = n < G ? n : (n < ncols ? n - G : -1);
+  // ---- query operand.  One token: column n holds head n, and for bf16/fp8
+  // head n-G again in columns G..2G-1, which carry the low half of P.  Two
+  // tokens (co-batched): column n holds token n/G, head n%G, and the low half
+  // of P takes a second MFMA.
+  constexpr bool LO_PACKED = NTOK == 1 && KV != KV_F32;
+  const int nq = NTOK * G;                    // query columns
+  const int ncols = LO_PACKED ? 2 * G : nq;   // columns holding a query
+  const int qc = n < nq ? n : (n < ncols ? n - G : -1);
+  const int tq = qc < 0 ? 0 : qc / G;         // this column's token
+  const int hq = qc < 0 ? -1 : qc % G;
   uint4 qop[KV == KV_F32 ? 1 : C::KS];
   float qopf[KV == KV_F32 ? C::KS : 1];
   {
-    const int64_t qrow = (((int64_t)b * p.T) * p.Hq + (int64_t)g * G + (hq < 0 ? 0 : hq)) * D;
+    const int64_t qrow = (((int64_t)b * p.T + tq) * p.Hq + (int64_t)g * G + (hq < 0 ? 0 : hq)) * D;
     if constexpr (KV == KV_F32) {
       // k-step s of group kg is element 16(s/4) + 4kg + s%4 of the row
       const float* qp = static_cast<const float*>(p.q) + qrow;
@@ -201,11 +215,13 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   char* vt = smem + w * C::PER_WAVE;
   uint4 kr[C::NT][C::GRAN];
   uint4 vr[C::NV];
-  int pos0 = 0;
+  int pos0 = 0, skip = 0;
   float ksc = 1.f, vsc = 1.f;
 
   // Issue the loads of the slice `sub` of `row` (pos0 already set).
   auto issue = [&](int row, int sub) {
+    skip = sub >> 8;
+    sub &= 0xff;
     // element offset of the slice, and its fp8 scales, from the source kind
     const bool win = pos0 < 0;
     const int kind = win ? p.window_kind : p.sparse_kind;
@@ -262,6 +278,8 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
     const int lo = win ? ws : 0;
     const int hi = win ? L : ws;
     const float ks_cur = ksc, vs_cur = vsc;
+    // a co-batched item that one token did not select is masked in that token's columns
+    const bool col_ok = NTOK == 1 || !((skip >> tq) & 1);
 
     // ---- S^T = K Q^T
     f32x4_t st[C::NT];
@@ -324,7 +342,7 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
       for (int r = 0; r < 4; ++r) {
         const int pos = p0 + 16 * tile + 4 * kg + r;
         float z = st[tile][r] * sc;
-        z = (pos >= lo && pos < hi) ? z : -INFINITY;
+        z = (pos >= lo && pos < hi && col_ok) ? z : -INFINITY;
         st[tile][r] = z;
         bm = fmaxf(bm, z);
       }
@@ -349,8 +367,8 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * kg + i;
-        const int head = row < ncols ? row % G : 0;
-        const float a = shfl_f(alpha, head);
+        const int col = row < ncols ? (row < nq ? row : row - G) : 0;
+        const float a = shfl_f(alpha, col);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) o[dt][i] *= a;
       }
@@ -364,7 +382,7 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
       for (int tile = 0; tile < C::NT; ++tile)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float a = n < G ? st[tile][r] : 0.f;
+          const float a = n < nq ? st[tile][r] : 0.f;
           const char* vrow = vt + (16 * tile + 4 * kg + r) * C::VROW + 4 * n;
 #pragma unroll
           for (int dt = 0; dt < C::DT; ++dt)
@@ -376,7 +394,7 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh) {
         // P operand: element e of lane (n, kg) is token 4kg + e%4 of tile 2hh + e/4
-        uint32_t pw[4];
+        uint32_t pw[4], plo[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           constexpr int NT = C::NT;
@@ -387,9 +405,11 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
           const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf16x2_t));
           const f32x2_t rest = {pv.x - bf16_lo(hw), pv.y - bf16_hi(hw)};
           const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_t));
-          pw[e2] = n < G ? hw : (n < ncols ? lw : 0u);
+          pw[e2] = n < nq ? hw : (n < ncols ? lw : 0u);
+          plo[e2] = n < nq ? lw : 0u;
         }
         const uint4 aop = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        const uint4 aop_lo = make_uint4(plo[0], plo[1], plo[2], plo[3]);
         // B operand: lane r of row group kg reads row 32hh + 4kg + r/4 (and +16),
         // columns 16dt + 4(r%4) .. +3; the transposing read hands lane n column
         // 16dt + n of those four rows, i.e. tokens 4kg .. 4kg+3 of each tile.
@@ -404,7 +424,9 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
                 (__attribute__((address_space(3))) i16x4_t*)(tbase + 16 * C::VROW + 32 * dt));
           const uint2 l2 = __builtin_bit_cast(uint2, lo4);
           const uint2 h2 = __builtin_bit_cast(uint2, hi4);
-          o[dt] = mfma_bf16(aop, make_uint4(l2.x, l2.y, h2.x, h2.y), o[dt]);
+          const uint4 bop = make_uint4(l2.x, l2.y, h2.x, h2.y);
+          o[dt] = mfma_bf16(aop, bop, o[dt]);
+          if constexpr (!LO_PACKED) o[dt] = mfma_bf16(aop_lo, bop, o[dt]);
         }
       }
     }
@@ -434,15 +456,20 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
 // `split` of n_splits; a single split writes the output directly, otherwise
 // the last split of (b, g) to arrive merges all of them.  `ready`, when given,
 // is the pair's ready flag, cleared once every split of the pair is done.
-template <int KV, int D, int BLK, int NW>
+// With NTOK query tokens the rows are (token, head) pairs and the output row
+// of token t, head h is (b, t, gG + h) of out [B][NTOK][Hq][d].
+template <int KV, int D, int BLK, int NW, int NTOK = 1>
 __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, int b, int g, int split,
                                               int n_splits, int* s_last, unsigned* ready) {
   using C = AttnCfg<KV, D, BLK>;
   constexpr int NTH = NW * kWave;
+  constexpr bool LO_PACKED = NTOK == 1 && KV != KV_F32;
   const int G = p.G;
+  const int NQ = NTOK * G;
   const int64_t pair = (int64_t)b * p.Hkv + g;
-  float* part = p.partials + (pair * n_splits + split) * G * (D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += NTH) {
+  auto out_row = [&](int c) { return ((int64_t)b * NTOK + c / G) * p.Hq + (int64_t)g * G + c % G; };
+  float* part = p.partials + (pair * n_splits + split) * NQ * (D + 2);
+  for (int idx = threadIdx.x; idx < NQ * D; idx += NTH) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
@@ -457,14 +484,14 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
         if (mw == -INFINITY) continue;
         const float f = exp2f(mw - M);
         float ov = comb[h * D + d];
-        if constexpr (KV != KV_F32) ov += comb[(G + h) * D + d];
+        if constexpr (LO_PACKED) ov += comb[(G + h) * D + d];
         O += f * ov;
         Ls += f * comb[16 * D + 16 + h];
       }
     }
     if (n_splits == 1) {
       // a single split is the whole attention of (b, g): write the result directly
-      const int64_t bh = (int64_t)b * p.Hq + (int64_t)g * G + h;
+      const int64_t bh = out_row(h);
       p.out[bh * D + d] = M == -INFINITY ? 0.f : O / Ls;
       if (d == 0 && p.lse) p.lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(Ls)) * kLn2;
       continue;
@@ -484,33 +511,34 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
   if (!arrive_last(p.counters + pair, (unsigned)n_splits, s_last)) return;
   // every split has passed its wait on the pair's ready flag: clear it for the next launch
   if (ready && threadIdx.x == 0) __hip_atomic_store(ready + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float* pb = p.partials + pair * n_splits * G * (D + 2);
-  // per (split, head): maxima and sums, then normalised weights 2^(m - M) / L
-  float* mm = reinterpret_cast<float*>(smem);   // [n_splits][G]
-  float* ll = mm + n_splits * G;                 // [n_splits][G]
-  float* wgt = ll + n_splits * G;                // [n_splits][G]
-  float* hres = wgt + n_splits * G;              // [G] lse in log2 units
-  for (int i = threadIdx.x; i < n_splits * G; i += NTH) {
-    const int s = i / G, h = i % G;
-    mm[i] = fetch_f32(pb + ((int64_t)s * G + h) * (D + 2));
-    ll[i] = fetch_f32(pb + ((int64_t)s * G + h) * (D + 2) + 1);
+  const float* pb = p.partials + pair * n_splits * NQ * (D + 2);
+  // per (split, row): maxima and sums, then normalised weights 2^(m - M) / L
+  // (the host keeps 3 n_splits NQ + NQ floats within the workgroup's LDS)
+  float* mm = reinterpret_cast<float*>(smem);   // [n_splits][NQ]
+  float* ll = mm + n_splits * NQ;                // [n_splits][NQ]
+  float* wgt = ll + n_splits * NQ;               // [n_splits][NQ]
+  float* hres = wgt + n_splits * NQ;             // [NQ] lse in log2 units
+  for (int i = threadIdx.x; i < n_splits * NQ; i += NTH) {
+    const int s = i / NQ, h = i % NQ;
+    mm[i] = fetch_f32(pb + ((int64_t)s * NQ + h) * (D + 2));
+    ll[i] = fetch_f32(pb + ((int64_t)s * NQ + h) * (D + 2) + 1);
   }
   __syncthreads();
-  if (threadIdx.x < G) {
+  if (threadIdx.x < NQ) {
     const int h = threadIdx.x;
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, mm[s * G + h]);
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, mm[s * NQ + h]);
     float Ls = 0.f;
     if (M != -INFINITY)
       for (int s = 0; s < n_splits; ++s)
-        if (mm[s * G + h] != -INFINITY) Ls += exp2f(mm[s * G + h] - M) * ll[s * G + h];
+        if (mm[s * NQ + h] != -INFINITY) Ls += exp2f(mm[s * NQ + h] - M) * ll[s * NQ + h];
     for (int s = 0; s < n_splits; ++s)
-      wgt[s * G + h] = (M == -INFINITY || mm[s * G + h] == -INFINITY) ? 0.f
-                                                                     : exp2f(mm[s * G + h] - M) / Ls;
+      wgt[s * NQ + h] = (M == -INFINITY || mm[s * NQ + h] == -INFINITY) ? 0.f
+                                                                       : exp2f(mm[s * NQ + h] - M) / Ls;
     hres[h] = M == -INFINITY ? -INFINITY : M + log2f(Ls);
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += NTH) {
+  for (int idx = threadIdx.x; idx < NQ * D; idx += NTH) {
     const int h = idx / D, d = idx % D;
     float acc = 0.f;
     constexpr int SB = 8;
@@ -518,12 +546,12 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
       float v[SB];
 #pragma unroll
       for (int u = 0; u < SB; ++u)
-        v[u] = (s0 + u < n_splits) ? fetch_f32(pb + ((int64_t)(s0 + u) * G + h) * (D + 2) + 2 + d) : 0.f;
+        v[u] = (s0 + u < n_splits) ? fetch_f32(pb + ((int64_t)(s0 + u) * NQ + h) * (D + 2) + 2 + d) : 0.f;
 #pragma unroll
       for (int u = 0; u < SB; ++u)
-        if (s0 + u < n_splits) acc += wgt[(s0 + u) * G + h] * v[u];
+        if (s0 + u < n_splits) acc += wgt[(s0 + u) * NQ + h] * v[u];
     }
-    const int64_t bh = (int64_t)b * p.Hq + (int64_t)g * G + h;
+    const int64_t bh = out_row(h);
     p.out[bh * D + d] = acc;
     if (d == 0 && p.lse) p.lse[bh] = hres[h] == -INFINITY ? -INFINITY : hres[h] * kLn2;
   }

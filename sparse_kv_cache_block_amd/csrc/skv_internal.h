@@ -46,7 +46,7 @@ struct TopkParams {
 // ------------------------------------------------------------------ attention
 struct AttnParams {
   int kv;                   // KvKind of K/V
-  const void* q;            // [B][T][Hq][d]; token 0 attended
+  const void* q;            // [B][T][Hq][d]; token 0 attended (both when co-batched)
   int B, T, Hq, Hkv, G, D, blk, window, max_blocks, k_max;
   float qk_scale;           // log2(e) / sqrt(d)
   // sparse part
@@ -68,13 +68,14 @@ struct AttnParams {
   const float* wvs;
   const int32_t* window_table;  // block table for a PAGED window
   const int32_t* seq_lens;
-  // split-K layout: workgroup s of (b, g) owns items [s*items_per_split, ...)
-  // of the concatenated list (sparse slices, then window slices)
+  // split-K layout: workgroup s of (b, g) owns items [s*n, (s+1)*n) of the
+  // concatenated list (sparse slices, then window slices), n = ceil(items of
+  // (b, g) / n_splits) <= items_per_split
   int n_splits, items_per_split;
-  float* partials;          // [B][Hkv][n_splits][G][d + 2]
+  float* partials;          // [B][Hkv][n_splits][tokens * G][d + 2]
   unsigned* counters;       // [B][Hkv]
-  float* out;               // [B][Hq][d]
-  float* lse;               // [B][Hq] or null
+  float* out;               // [B][Hq][d]; co-batched [B][2][Hq][d]
+  float* lse;               // [B][Hq] or null; co-batched [B][2][Hq]
   int longest_first;        // single-launch step: workgroup row r takes the sequence of
                             // length rank r (descending), so long pairs start first
 };
@@ -114,6 +115,7 @@ struct Plan {
   int max_cand;             // upper bound of candidates per sequence
   int rows_per_chunk, score_chunks;
   int items_per_split, n_splits;   // attention split-K
+  int cob_items_per_split, cob_n_splits;   // co-batched two-token attention (T = 2)
   // single-launch step: one workgroup per (sequence, KV head) scores,
   // selects and attends (fused_step = 1 when the shape has that kernel and
   // there are enough pairs to fill the chip)
@@ -127,6 +129,14 @@ Plan make_plan(const skv_problem& pr);
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(const AttnParams& p, hipStream_t s);
+// Co-batched attention of both query tokens (T = 2, paged sparse source).
+hipError_t launch_attend_cobatched(const AttnParams& p, hipStream_t s);
+// Static LDS bytes of an attention workgroup (kv: KvKind); its split merge
+// keeps 3 n_splits (tokens G) + tokens G floats there.
+size_t attend_lds_bytes(int kv, int D, int blk);
+// Union blocks one co-batched split can cover: its items per split stay at
+// most (this - 1) * items per block.
+constexpr int kCobatchMaxSplitBlocks = 130;
 hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hipStream_t st);
 // Whether a step kernel is built for this shape (device pool, d = 128, bf16
 // queries and landmarks, bf16 or fp8 K/V, blocks of 32 or 64 tokens).

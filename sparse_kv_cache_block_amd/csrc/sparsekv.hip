@@ -129,6 +129,17 @@ Plan make_plan(const skv_problem& p) {
   pl.items_per_split = ips;
   pl.n_splits = (total_items + ips - 1) / ips;
   const int total = pl.n_splits;
+  // co-batched attention of two tokens: the list holds up to 2 k_max union
+  // blocks; a split covers at most kCobatchMaxSplitBlocks - 2 blocks' items
+  size_t part_rows = (size_t)total * G;
+  if (p.n_q_tokens == 2) {
+    const int cob_items = (2 * p.k_max + nwb) * sub;
+    int ips2 = (int)(((int64_t)pairs * cob_items + kAttnTargetWorkgroups - 1) / kAttnTargetWorkgroups);
+    ips2 = std::max(16, std::min(ips2, (kCobatchMaxSplitBlocks - 2) * sub));
+    pl.cob_items_per_split = ips2;
+    pl.cob_n_splits = (cob_items + ips2 - 1) / ips2;
+    part_rows = std::max(part_rows, (size_t)pl.cob_n_splits * 2 * G);
+  }
 
   // single-launch step
   pl.fused_step = 0;
@@ -147,7 +158,7 @@ Plan make_plan(const skv_problem& p) {
   pl.off_scores = off;
   off = align256(off + (size_t)pairs * p.n_q_tokens * (pl.max_cand > 0 ? pl.max_cand : 1) * 4);
   pl.off_partials = off;
-  off = align256(off + (size_t)pairs * total * G * (D + 2) * 4);
+  off = align256(off + (size_t)pairs * part_rows * (D + 2) * 4);
   pl.off_phys = off;
   off = align256(off + (size_t)pairs * p.n_q_tokens * p.k_max * 4);
   pl.total_bytes = off;
@@ -579,6 +590,42 @@ skv_status sparsekv_attend(const skv_problem* pr, const void* q, const skv_kv_so
   a.indices = indices;
   a.n_sel = n_sel;
   SKV_TRY_HIP(launch_attend(a, as_stream(stream)), "attention launch");
+  return SKV_OK;
+}
+
+skv_status sparsekv_attend_cobatched(const skv_problem* pr, const void* q, const skv_kv_source* sparse,
+                                     const int32_t* indices, const int32_t* n_sel,
+                                     const skv_kv_source* window, const int32_t* seq_lens, float* out,
+                                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  // one token: the output layouts coincide with sparsekv_attend's
+  if (p.n_q_tokens == 1)
+    return sparsekv_attend(pr, q, sparse, indices, n_sel, window, seq_lens, out, lse, workspace,
+                           workspace_bytes, stream);
+  if (!q || !indices || !n_sel || !seq_lens || !out) return fail(SKV_E_NULL, "attend_cobatched: NULL argument");
+  if (!sparse) return fail(SKV_E_NULL, "sparse source is NULL");
+  if (sparse->kind != SKV_SRC_PAGED)
+    return fail(SKV_E_UNSUPPORTED, "attend_cobatched reads the union of the selections from a paged source");
+  if (p.pool_location != SKV_POOL_DEVICE)
+    return fail(SKV_E_UNSUPPORTED, "attend_cobatched needs a device pool");
+  const Plan pl = make_plan(p);
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  const int G = p.n_q_heads / p.n_kv_heads;
+  const size_t merge_bytes = ((size_t)3 * pl.cob_n_splits + 1) * 2 * G * 4;
+  if (merge_bytes > attend_lds_bytes(kv_kind(p.kv_dtype), p.head_dim, p.block_size))
+    return fail(SKV_E_UNSUPPORTED, "attend_cobatched: %d splits of %d items exceed the merge's LDS",
+                pl.cob_n_splits, pl.cob_items_per_split);
+  char* ws = static_cast<char*>(workspace);
+  AttnParams a = attn_params(p, pl, q, seq_lens, out, lse, ws);
+  a.n_splits = pl.cob_n_splits;
+  a.items_per_split = pl.cob_items_per_split;
+  SKV_TRY(set_source(p, a, sparse, true));
+  if (p.window > 0) SKV_TRY(set_source(p, a, window, false));
+  else a.window_kind = SKV_SRC_WINDOW;
+  a.indices = indices;
+  a.n_sel = n_sel;
+  SKV_TRY_HIP(launch_attend_cobatched(a, as_stream(stream)), "co-batched attention launch");
   return SKV_OK;
 }
 

@@ -245,8 +245,9 @@ def test_gather_equals_fancy_indexing_and_round_trips():
 
 
 # --------------------------------------------------------------- attention
-def _numpy_dense(inp, b, hq, positions):
-    """Independent brute force: softmax(q.k/sqrt(d)) v over positions, numpy fp64."""
+def _numpy_dense(inp, b, hq, positions, t=0):
+    """Independent brute force: softmax(q.k/sqrt(d)) v over positions, numpy fp64
+    (query token t)."""
     wl = inp.wl
     blk = wl.block_size
     g = hq // wl.group
@@ -259,7 +260,7 @@ def _numpy_dense(inp, b, hq, positions):
         kk, vv = K[g, phys, rows], V[g, phys, rows]
     else:
         kk, vv = K[phys, g, rows], V[phys, g, rows]
-    q = inp.q.double().numpy()[b, 0, hq]
+    q = inp.q.double().numpy()[b, t, hq]
     z = kk @ q / math.sqrt(wl.head_dim)
     m = z.max()
     w = np.exp(z - m)
@@ -426,3 +427,46 @@ def test_overlap_identical_and_disjoint():
     pr1 = O.problem(1, 2, 1, 1, 1, 1, 16, 16, 1, 1, 0, 4, "bf16", "bf16", "bf16")
     ov = O.overlap(pr1, idx, np.array([[[4], [3]]], np.int32))
     assert ov[0, 0] == 0.5
+
+
+# --------------------------------------------------------------- both query tokens
+def _dual_small(**kw):
+    return configs.DUAL.scaled(batch=2, context=1500, n_q_heads=16, n_kv_heads=2, window=100, top_k=6, **kw)
+
+
+def test_attend_tokens_vs_numpy_brute_force():
+    # each token attends its own selection plus the window (co-batched attention)
+    wl = _dual_small()
+    inp = make_inputs(wl)
+    h = HostArrays(inp)
+    pr = oracle_problem(inp)
+    r = O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
+    out, lse = O.attend_tokens(pr, h.q, *h.pools(), h.block_table, h.seq_lens, r["indices"], r["n_sel"])
+    assert not np.array_equal(r["indices"][:, 0], r["indices"][:, 1])
+    blk, G = wl.block_size, wl.group
+    for b in range(wl.batch):
+        L = int(h.seq_lens[b])
+        ws = max(0, L - wl.window)
+        for t in range(2):
+            for hq in (0, 7, 8, 15):
+                sel = r["indices"][b, t, hq // G, :int(r["n_sel"][b, t, hq // G])]
+                pos = [j * blk + x for j in sel for x in range(blk) if j * blk + x < ws] + list(range(ws, L))
+                o, ls = _numpy_dense(inp, b, hq, np.array(pos), t=t)
+                np.testing.assert_allclose(out[b, t, hq], o, atol=1e-12, rtol=0)
+                assert lse[b, t, hq] == pytest.approx(ls, abs=1e-12)
+
+
+def test_attend_tokens_swapping_tokens_swaps_results():
+    wl = _dual_small()
+    inp = make_inputs(wl)
+    h = HostArrays(inp)
+    pr = oracle_problem(inp)
+    r = O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
+    out, lse = O.attend_tokens(pr, h.q, *h.pools(), h.block_table, h.seq_lens, r["indices"], r["n_sel"])
+    q_sw = np.ascontiguousarray(h.q[:, ::-1])
+    idx_sw = np.ascontiguousarray(r["indices"][:, ::-1])
+    nsel_sw = np.ascontiguousarray(r["n_sel"][:, ::-1])
+    out_sw, lse_sw = O.attend_tokens(pr, q_sw, *h.pools(), h.block_table, h.seq_lens, idx_sw, nsel_sw)
+    assert np.array_equal(out_sw[:, 0], out[:, 1]) and np.array_equal(out_sw[:, 1], out[:, 0])
+    assert np.array_equal(lse_sw[:, ::-1], lse)
+    assert not np.allclose(out[:, 0], out[:, 1])

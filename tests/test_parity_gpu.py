@@ -285,6 +285,103 @@ def test_gather_and_attend_entry_points():
         assert (lse2 - st.lse).abs().max().item() <= 2e-5
 
 
+# ------------------------------------------------ co-batched two-token attention
+def _two_token_attention(st):
+    """Co-batched attention of both tokens, and the two single-token launches
+    it replaces (token 1 through views that start at its rows)."""
+    dev, pr = st.inp, st.pr
+    Bn, Hq, D = dev.q.shape[0], dev.q.shape[2], dev.q.shape[3]
+    out = torch.full((Bn, 2, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((Bn, 2, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    src = B.kv_source(B.SKV_SRC_PAGED, dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales, dev.block_table)
+    B.sparsekv_attend_cobatched(pr, dev.q, src, st.indices, st.n_sel, src, dev.seq_lens, out, lse, st.ws)
+    sep_out = torch.empty_like(out)
+    sep_lse = torch.empty_like(lse)
+    for t in range(2):
+        o_t = torch.empty((Bn, Hq, D), dtype=torch.float32, device="cuda")
+        l_t = torch.empty((Bn, Hq), dtype=torch.float32, device="cuda")
+        B.sparsekv_attend(pr, dev.q[:, t:], src, st.indices[:, t:], st.n_sel[:, t:], src, dev.seq_lens,
+                          o_t, l_t, st.ws)
+        sep_out[:, t] = o_t
+        sep_lse[:, t] = l_t
+    torch.cuda.synchronize()
+    return out, lse, sep_out, sep_lse
+
+
+def check_cobatched(wl, seq_lens=None, mutate=None):
+    announce(f"attend_cobatched {wl.name} B={wl.batch} L={wl.context} Hq={wl.n_q_heads} Hkv={wl.n_kv_heads} "
+             f"d={wl.head_dim} blk={wl.block_size} k={wl.top_k} W={wl.window} kv={wl.kv_dtype} "
+             f"seq_lens={seq_lens}")
+    inp, st = run_step(wl, seq_lens=seq_lens, mutate=mutate)
+    out, lse, sep_out, sep_lse = _two_token_attention(st)
+    h = HostArrays(inp)
+    gi, gn = _np(st.indices), _np(st.n_sel)
+    pr = oracle_problem(inp, k_max=gi.shape[-1])
+    o_out, o_lse = O.attend_tokens(pr, h.q, *h.pools(), h.block_table, h.seq_lens, gi, gn)
+    tol = TOL[wl.kv_dtype]
+    g_out, g_lse = _np(out), _np(lse)
+    err = float(np.max(np.abs(g_out.astype(np.float64) - o_out)))
+    assert err <= tol, f"co-batched attention max-abs error {err} > {tol}"
+    fin = np.isfinite(o_lse)
+    assert np.array_equal(fin, np.isfinite(g_lse))
+    assert np.all(g_lse[~fin] == -np.inf)
+    if fin.any():
+        assert float(np.max(np.abs(g_lse[fin] - o_lse[fin]))) <= tol
+    # the same values as one launch per token, and as the decode step's real token
+    assert (out - sep_out).abs().max().item() <= 2e-5
+    if fin.any():
+        fin_t = torch.from_numpy(fin).cuda()
+        assert (lse[fin_t] - sep_lse[fin_t]).abs().max().item() <= 2e-5
+    assert (out[:, 0] - st.out).abs().max().item() <= 2e-5
+    union = sum(len(set(gi[b, 0, g, :gn[b, 0, g]]) | set(gi[b, 1, g, :gn[b, 1, g]]))
+                for b in range(gi.shape[0]) for g in range(gi.shape[2]))
+    print(f"[case] ok: max-abs err {err:.3g}, union blocks {union}", flush=True)
+    return out, st
+
+
+@pytest.mark.parametrize("wl,lens", [
+    (configs.DUAL.scaled(batch=2, context=8192, top_k=30), None),                  # G = 8 fp8, 16 columns
+    (configs.DUAL.scaled(batch=3, context=4096, block_size=32, top_k=20, window=256), [4096, 700, 0]),
+    (configs.LLAMA32K.scaled(batch=2, context=4096, n_q_tokens=2, spec_noise=0.3), None),   # G = 4 bf16
+    (configs.LLAMA32K.scaled(batch=2, context=3000, n_q_tokens=2, spec_noise=0.3, block_size=16,
+                             head_dim=64, window=0), [3000, 1]),
+    (configs.TINY.scaled(n_q_tokens=2, spec_noise=0.3), None),                      # fp32
+])
+def test_cobatched_attention(wl, lens):
+    check_cobatched(wl, seq_lens=lens)
+
+
+def test_cobatched_identical_and_disjoint_tokens():
+    wl = configs.DUAL.scaled(batch=2, context=8192, top_k=30)
+
+    def same(inp):
+        inp.q[:, 1] = inp.q[:, 0]
+    out, st = check_cobatched(wl, mutate=same)
+    assert (out[:, 0] - out[:, 1]).abs().max().item() <= 1e-6
+
+    def opposite(inp):
+        inp.q[:, 1] = -inp.q[:, 0]
+    # reversed ranking: the union holds 2k blocks per (sequence, KV head)
+    check_cobatched(wl, mutate=opposite)
+    # k beyond the candidates: both tokens select every candidate
+    check_cobatched(wl.scaled(top_k=120))
+
+
+def test_cobatched_full_size_dual():
+    check_cobatched(configs.DUAL)
+
+
+def test_cobatched_rejects_staged_and_host():
+    wl = configs.DUAL.scaled(batch=2, context=4096, top_k=10)
+    inp, st = run_step(wl)
+    dev, pr = st.inp, st.pr
+    src = B.kv_source(B.SKV_SRC_STAGED, dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales)
+    win = B.kv_source(B.SKV_SRC_PAGED, dev.k_pool, dev.v_pool, dev.k_scales, dev.v_scales, dev.block_table)
+    out = torch.empty((2, 2, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+    with pytest.raises(RuntimeError, match="paged"):
+        B.sparsekv_attend_cobatched(pr, dev.q, src, st.indices, st.n_sel, win, dev.seq_lens, out, None, st.ws)
+
+
 @pytest.mark.parametrize("wl", [configs.DUAL.scaled(batch=2, context=8192, top_k=30),
                                 configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3)])
 def test_speculative_gather_correction(wl):
