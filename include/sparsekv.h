@@ -252,8 +252,7 @@ skv_status sparsekv_attend(const skv_problem *pr, const void *q, const skv_kv_so
  * token selected is masked for the other.  out is [B][T][Hq][d] fp32, lse
  * [B][T][Hq] (may be NULL).  T == 2 needs a device pool and a PAGED sparse
  * source (the union is read through the block table); SKV_E_UNSUPPORTED
- * otherwise, and for k_max large enough that the split merge would not fit
- * in a workgroup's LDS.  T == 1 is sparsekv_attend.  The workspace is the
+ * otherwise.  T == 1 is sparsekv_attend.  The workspace is the
  * one sparsekv_workspace_size gives for the problem.
  */
 skv_status sparsekv_attend_cobatched(const skv_problem *pr, const void *q,

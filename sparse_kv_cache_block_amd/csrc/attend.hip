@@ -192,20 +192,4 @@ hipError_t launch_attend(const AttnParams& p, hipStream_t s) { return launch_kin
 
 hipError_t launch_attend_cobatched(const AttnParams& p, hipStream_t s) { return launch_kind(p, s, true); }
 
-size_t attend_lds_bytes(int kv, int D, int blk) {
-  auto pick = [&](auto kvc) -> size_t {
-    constexpr int K = decltype(kvc)::value;
-    if (D == 128) return blk == 16 ? attn_lds_bytes<K, 128, 16>(kAttnWaves)
-                                   : blk == 32 ? attn_lds_bytes<K, 128, 32>(kAttnWaves)
-                                               : attn_lds_bytes<K, 128, 64>(kAttnWaves);
-    return blk == 16 ? attn_lds_bytes<K, 64, 16>(kAttnWaves)
-                     : blk == 32 ? attn_lds_bytes<K, 64, 32>(kAttnWaves) : attn_lds_bytes<K, 64, 64>(kAttnWaves);
-  };
-  switch (kv) {
-    case KV_F32: return pick(std::integral_constant<int, KV_F32>{});
-    case KV_BF16: return pick(std::integral_constant<int, KV_BF16>{});
-    default: return pick(std::integral_constant<int, KV_FP8>{});
-  }
-}
-
 }  // namespace skv

@@ -511,49 +511,44 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
   if (!arrive_last(p.counters + pair, (unsigned)n_splits, s_last)) return;
   // every split has passed its wait on the pair's ready flag: clear it for the next launch
   if (ready && threadIdx.x == 0) __hip_atomic_store(ready + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // each thread merges its outputs over the splits online, reading 8 splits'
+  // (max, sum, output) per round of loads: one round for up to 8 splits, and
+  // no LDS whatever the split count
   const float* pb = p.partials + pair * n_splits * NQ * (D + 2);
-  // per (split, row): maxima and sums, then normalised weights 2^(m - M) / L
-  // (the host keeps 3 n_splits NQ + NQ floats within the workgroup's LDS)
-  float* mm = reinterpret_cast<float*>(smem);   // [n_splits][NQ]
-  float* ll = mm + n_splits * NQ;                // [n_splits][NQ]
-  float* wgt = ll + n_splits * NQ;               // [n_splits][NQ]
-  float* hres = wgt + n_splits * NQ;             // [NQ] lse in log2 units
-  for (int i = threadIdx.x; i < n_splits * NQ; i += NTH) {
-    const int s = i / NQ, h = i % NQ;
-    mm[i] = fetch_f32(pb + ((int64_t)s * NQ + h) * (D + 2));
-    ll[i] = fetch_f32(pb + ((int64_t)s * NQ + h) * (D + 2) + 1);
-  }
-  __syncthreads();
-  if (threadIdx.x < NQ) {
-    const int h = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, mm[s * NQ + h]);
-    float Ls = 0.f;
-    if (M != -INFINITY)
-      for (int s = 0; s < n_splits; ++s)
-        if (mm[s * NQ + h] != -INFINITY) Ls += exp2f(mm[s * NQ + h] - M) * ll[s * NQ + h];
-    for (int s = 0; s < n_splits; ++s)
-      wgt[s * NQ + h] = (M == -INFINITY || mm[s * NQ + h] == -INFINITY) ? 0.f
-                                                                       : exp2f(mm[s * NQ + h] - M) / Ls;
-    hres[h] = M == -INFINITY ? -INFINITY : M + log2f(Ls);
-  }
-  __syncthreads();
   for (int idx = threadIdx.x; idx < NQ * D; idx += NTH) {
     const int h = idx / D, d = idx % D;
-    float acc = 0.f;
+    float M = -INFINITY, Ls = 0.f, acc = 0.f;
     constexpr int SB = 8;
     for (int s0 = 0; s0 < n_splits; s0 += SB) {
-      float v[SB];
+      float mv[SB], lv[SB], ov[SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u)
-        v[u] = (s0 + u < n_splits) ? fetch_f32(pb + ((int64_t)(s0 + u) * NQ + h) * (D + 2) + 2 + d) : 0.f;
+      for (int u = 0; u < SB; ++u) {
+        const bool in = s0 + u < n_splits;
+        const float* ps = pb + ((int64_t)(in ? s0 + u : s0) * NQ + h) * (D + 2);
+        mv[u] = fetch_f32(ps);
+        lv[u] = fetch_f32(ps + 1);
+        ov[u] = fetch_f32(ps + 2 + d);
+        if (!in) mv[u] = -INFINITY;
+      }
+      float Mc = M;
 #pragma unroll
-      for (int u = 0; u < SB; ++u)
-        if (s0 + u < n_splits) acc += wgt[(s0 + u) * NQ + h] * v[u];
+      for (int u = 0; u < SB; ++u) Mc = fmaxf(Mc, mv[u]);
+      if (Mc == -INFINITY) continue;
+      const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);
+      Ls *= r;
+      acc *= r;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        if (mv[u] == -INFINITY) continue;
+        const float f = exp2f(mv[u] - Mc);
+        Ls += f * lv[u];
+        acc += f * ov[u];
+      }
+      M = Mc;
     }
     const int64_t bh = out_row(h);
-    p.out[bh * D + d] = acc;
-    if (d == 0 && p.lse) p.lse[bh] = hres[h] == -INFINITY ? -INFINITY : hres[h] * kLn2;
+    p.out[bh * D + d] = M == -INFINITY ? 0.f : acc / Ls;
+    if (d == 0 && p.lse) p.lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(Ls)) * kLn2;
   }
 }
 

@@ -131,9 +131,6 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t s);
 hipError_t launch_attend(const AttnParams& p, hipStream_t s);
 // Co-batched attention of both query tokens (T = 2, paged sparse source).
 hipError_t launch_attend_cobatched(const AttnParams& p, hipStream_t s);
-// Static LDS bytes of an attention workgroup (kv: KvKind); its split merge
-// keeps 3 n_splits (tokens G) + tokens G floats there.
-size_t attend_lds_bytes(int kv, int D, int blk);
 // Union blocks one co-batched split can cover: its items per split stay at
 // most (this - 1) * items per block.
 constexpr int kCobatchMaxSplitBlocks = 130;

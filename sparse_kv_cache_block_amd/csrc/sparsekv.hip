@@ -611,11 +611,6 @@ skv_status sparsekv_attend_cobatched(const skv_problem* pr, const void* q, const
     return fail(SKV_E_UNSUPPORTED, "attend_cobatched needs a device pool");
   const Plan pl = make_plan(p);
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
-  const int G = p.n_q_heads / p.n_kv_heads;
-  const size_t merge_bytes = ((size_t)3 * pl.cob_n_splits + 1) * 2 * G * 4;
-  if (merge_bytes > attend_lds_bytes(kv_kind(p.kv_dtype), p.head_dim, p.block_size))
-    return fail(SKV_E_UNSUPPORTED, "attend_cobatched: %d splits of %d items exceed the merge's LDS",
-                pl.cob_n_splits, pl.cob_items_per_split);
   char* ws = static_cast<char*>(workspace);
   AttnParams a = attn_params(p, pl, q, seq_lens, out, lse, ws);
   a.n_splits = pl.cob_n_splits;
