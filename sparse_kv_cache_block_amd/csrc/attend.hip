@@ -27,9 +27,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   const int first = split * ips;
   const int count = max(0, min(ips, total - first));
   attend_items<KV, D, BLK, kAttnWaves>(
-      p, smem, b, g, first, count, [&](int item) { return describe<KV, D, BLK>(p, b, g, item, nsel, ws); },
-      [](int) { return ItemDesc{0, 0, 0}; }, [](int) { return true; },
-      [](auto&& issue_first) { issue_first(); }, [] {});
+      p, smem, b, g, first, count, count, 0,
+      [&](int item) { return describe<KV, D, BLK>(p, b, g, item, nsel, ws); },
+      [](int) { return ItemDesc{0, 0, 0}; }, [] {}, [](auto&& issue_first) { issue_first(); }, [] {});
   attend_finish<KV, D, BLK, kAttnWaves>(p, smem, b, g, split, p.n_splits, &s_last, nullptr);
 }
 
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_cobatched_kernel(AttnPara
       kCobatchMaxSplitBlocks, tab, &scan_w[0][0], reinterpret_cast<int32_t*>(smem), (int)(sizeof(smem) / 4));
   const int r0 = first / C::SUB;
   attend_items<KV, D, BLK, kAttnWaves, 2>(
-      p, smem, b, g, first, count,
+      p, smem, b, g, first, count, count, 0,
       [&](int item) {
         const int bi = item / C::SUB, sub = item % C::SUB;
         if (bi < nu) {
@@ -151,8 +151,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_cobatched_kernel(AttnPara
         }
         return describe_window<KV, D, BLK>(p, b, g, bi - nu, sub, ws);
       },
-      [](int) { return ItemDesc{0, 0, 0}; }, [](int) { return true; },
-      [](auto&& issue_first) { issue_first(); }, [] {});
+      [](int) { return ItemDesc{0, 0, 0}; }, [] {}, [](auto&& issue_first) { issue_first(); }, [] {});
   attend_finish<KV, D, BLK, kAttnWaves, 2>(p, smem, b, g, split, p.n_splits, &s_last, nullptr);
 }
 

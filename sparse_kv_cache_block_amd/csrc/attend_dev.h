@@ -76,6 +76,13 @@ struct ItemDesc {
   int sub;        // slice of the block (bits 0-7); bits 8-9: query tokens that skip the item
 };
 
+// Slice `sub` of block j of a paged source whose physical block is known.
+template <int KV, int D, int BLK>
+__device__ __forceinline__ ItemDesc describe_paged(int j, int phys, int sub) {
+  using C = AttnCfg<KV, D, BLK>;
+  return ItemDesc{phys, j * BLK + sub * C::TB, sub};
+}
+
 // Slice `sub` of the m-th selected block of (b, g), block id j.  A paged
 // source reads physical block `phys` (negative: look it up in the block
 // table); a staged source reads slot m of the (b, g) staging row.
@@ -138,22 +145,30 @@ __device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws)
 }
 
 // One NW-wave workgroup's attention of (b, g) over items [first, first+count)
-// of its list.  Wave w takes items first + w, first + w + NW, ...; lane j of
-// the wave holds the descriptor of the wave's j-th item.  Items for which
-// early(item) holds are described by desc_early before the hooks, the others
-// by desc_late after them; both are called for every lane with an item of
-// the list (clamped), so they must accept any of them.  pre(issue_first) runs
-// once the query loads are issued and must call issue_first() exactly once,
-// which issues the loads of the wave's first item if that item is early (a
-// wave without one issues the same loads from row 0 of its source, so every
-// path has the same count of loads in flight); post() runs after pre (both
-// hooks run in every thread).  Leaves each wave's unnormalised O rows,
-// running max and sum in its LDS combine region.
-template <int KV, int D, int BLK, int NW, int NTOK = 1, class EarlyDescFn, class LateDescFn, class EarlyFn,
-          class PreFn, class PostFn>
+// of its list.  The first n_early items are early: described by desc_early
+// before the hooks and taken in turn by waves early_wave0 .. NW-1.  The rest
+// are late: taken in turn by all NW waves (with DYN_LATE: taken one at a
+// time, by whichever wave needs one next, from the LDS counter *late_next,
+// which starts at 0) and described by desc_late, in a wave only once
+// late_ready() has returned in it (late_ready waits until late descriptors
+// can be formed).  A wave works through its early items, then its late ones;
+// lane j of the wave holds the descriptor of the wave's j-th item, so a wave
+// takes at most 64 statically assigned items.  The descriptor functions are
+// called for the lanes past a wave's items with its last item of that kind,
+// and never for an item outside the list.  pre(issue_first) runs once the
+// query loads are issued and must call issue_first() exactly once, which
+// issues the loads of the wave's first item if that item is early.  With
+// PAD_FIRST a wave without one issues the same loads from row 0 of its
+// source, so every path has the same count of loads in flight; without it
+// such a wave issues nothing and reaches post() at once.  post() runs after
+// pre (both hooks run in every thread).  Leaves each wave's unnormalised O rows, running max
+// and sum in its LDS combine region.
+template <int KV, int D, int BLK, int NW, int NTOK = 1, bool PAD_FIRST = true, bool DYN_LATE = false,
+          class EarlyDescFn, class LateDescFn, class LateReadyFn, class PreFn, class PostFn>
 __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, int b, int g, int first,
-                                             int count, EarlyDescFn desc_early, LateDescFn desc_late,
-                                             EarlyFn early, PreFn pre, PostFn post) {
+                                             int count, int n_early, int early_wave0, EarlyDescFn desc_early,
+                                             LateDescFn desc_late, LateReadyFn late_ready, PreFn pre,
+                                             PostFn post, int* late_next = nullptr) {
   using C = AttnCfg<KV, D, BLK>;
   const int lane = lane_id(), w = wave_id();
   const int n = lane & 15;   // C/B column, A row
@@ -193,14 +208,22 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
     }
   }
 
-  const int my_items = count > w ? (count - w + NW - 1) / NW : 0;  // this wave's items
-  const int my_item = min(first + w + NW * lane, first + count - 1);
-
+  // this wave's items: early ones strided over waves early_wave0 .. NW-1,
+  // then late ones strided over every wave
+  const int ew = NW - early_wave0, we = w - early_wave0;
+  const int n_late = count - n_early;
+  const int my_early = (we >= 0 && n_early > we) ? (n_early - we + ew - 1) / ew : 0;
+  const int my_late = DYN_LATE ? 0 : (n_late > w ? (n_late - w + NW - 1) / NW : 0);
+  int my_items = my_early + my_late;   // with DYN_LATE it grows as late items are taken
   // lane j describes this wave's item j; early and late descriptors stay in
   // separate registers, so reading an early item never waits for the loads
   // behind a late one
   ItemDesc d_early{0, 0, 0}, d_late{0, 0, 0};
-  if (count > 0) d_early = desc_early(my_item);
+  if (my_early > 0) d_early = desc_early(first + we + ew * min(lane, my_early - 1));
+  auto describe_late = [&] {
+    late_ready();
+    d_late = desc_late(first + n_early + w + NW * min(max(lane - my_early, 0), my_late - 1));
+  };
 
   const char* kbase_s = static_cast<const char*>(p.sk);
   const char* vbase_s = static_cast<const char*>(p.sv);
@@ -252,7 +275,7 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   // Issue the loads of the wave's item j (descriptor broadcast from lane j;
   // scalar selects between the early and late descriptors).
   auto load_item = [&](int j) {
-    const bool e = early(first + w + NW * j);
+    const bool e = j < my_early;
     const int re = __builtin_amdgcn_readlane(d_early.row, j), rl = __builtin_amdgcn_readlane(d_late.row, j);
     const int pe = __builtin_amdgcn_readlane(d_early.pos0, j), pl = __builtin_amdgcn_readlane(d_late.pos0, j);
     const int se = __builtin_amdgcn_readlane(d_early.sub, j), sl = __builtin_amdgcn_readlane(d_late.sub, j);
@@ -260,17 +283,39 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
     issue(e ? re : rl, e ? se : sl);
   };
 
-  const bool first_early = my_items > 0 && early(first + w);
+  const bool first_early = my_early > 0;
   pre([&] {
     const int r0 = __builtin_amdgcn_readlane(d_early.row, 0);
     const int s0 = __builtin_amdgcn_readlane(d_early.sub, 0);
     const int p0 = __builtin_amdgcn_readlane(d_early.pos0, 0);
-    pos0 = first_early ? p0 : 0;
-    issue(first_early ? r0 : 0, first_early ? s0 : 0);
+    if (PAD_FIRST || first_early) {
+      pos0 = first_early ? p0 : 0;
+      issue(first_early ? r0 : 0, first_early ? s0 : 0);
+    }
   });
+  // DYN_LATE: take the next late item and issue its loads; false when none is left
+  bool late_open = false;
+  auto take_late = [&]() -> bool {
+    if (!late_open) {
+      late_ready();
+      late_open = true;
+    }
+    int v = 0;
+    if (lane == 0) v = atomicAdd(late_next, 1);
+    v = __builtin_amdgcn_readfirstlane(v);
+    if (v >= n_late) return false;
+    const ItemDesc d = desc_late(first + n_early + v);
+    pos0 = __builtin_amdgcn_readfirstlane(d.pos0);
+    issue(__builtin_amdgcn_readfirstlane(d.row), __builtin_amdgcn_readfirstlane(d.sub));
+    return true;
+  };
   post();
-  if (count > 0) d_late = desc_late(my_item);
-  if (my_items > 0 && !first_early) load_item(0);
+  if constexpr (DYN_LATE) {
+    if (!first_early && take_late()) my_items = 1;
+  } else if (!first_early && my_late > 0) {
+    describe_late();
+    load_item(0);
+  }
 
   for (int j = 0; j < my_items; ++j) {
     const bool win = pos0 < 0;
@@ -331,7 +376,13 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
     }
 
     // ---- prefetch the next item while this one finishes
-    if (j + 1 < my_items) load_item(j + 1);
+    if constexpr (DYN_LATE) {
+      if (j + 1 < my_early) load_item(j + 1);
+      else if (take_late()) ++my_items;
+    } else if (j + 1 < my_items) {
+      if (j + 1 == my_early) describe_late();
+      load_item(j + 1);
+    }
 
     // ---- online softmax (log2 domain)
     const float sc = p.qk_scale * ks_cur;

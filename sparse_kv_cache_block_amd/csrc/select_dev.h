@@ -201,6 +201,116 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
   return nsel;
 }
 
+// The same selection made by one wave alone, with no workgroup barrier, so
+// the workgroup's other waves can do other work meanwhile.  hist is the
+// wave's own 256-bin LDS histogram; keys, hist0 and lds_out as in
+// block_select.  Keys are read 8 per lane before they are used, so a pass
+// waits for LDS about once per 512 keys; the chosen indices are emitted in
+// ascending order 64 at a time with ballots.  Returns k'.
+__device__ __forceinline__ int wave_select(const uint32_t* keys, int n, int k, int k_max, int32_t* lds_out,
+                                           uint32_t* hist, const uint32_t* hist0 = nullptr) {
+  constexpr int U = 8;  // keys per lane per round of LDS reads
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+  int kk = k < n ? k : n;
+  if (kk > k_max) kk = k_max;
+  if (kk < 0) kk = 0;
+  const bool take_all = kk >= n;
+  uint32_t thresh = 0, take_eq = 0;
+  if (!take_all && kk > 0) {
+    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)kk;
+    bool at_or_above = false;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      const uint32_t* h = hist;
+      if (pass == 0 && hist0) {
+        h = hist0;
+      } else {
+        for (int t = lane; t < 256; t += kWave) hist[t] = 0;
+        wave_lds_sync();
+        for (int j0 = 0; j0 < n; j0 += U * kWave) {
+          uint32_t kv[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * kWave + lane;
+            kv[u] = keys[j < n ? j : 0];
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * kWave + lane;
+            if (j < n && (kv[u] & pmask) == prefix) atomicAdd(&hist[(kv[u] >> shift) & 255u], 1u);
+          }
+        }
+        wave_lds_sync();
+      }
+      // lane l owns digits 255-4l .. 252-4l (descending); exactly one lane
+      // holds the digit of the k'-th largest matching key
+      uint32_t c[4], lsum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = h[255 - 4 * lane - i];
+        lsum += c[i];
+      }
+      uint32_t above = wave_inclusive_scan(lsum) - lsum;
+      int my_digit = -1;
+      uint32_t my_above = 0, my_exact = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < remaining && above + c[i] >= remaining) {
+          my_digit = 255 - 4 * lane - i;
+          my_above = above;
+          my_exact = above + c[i] == remaining;
+        }
+        above += c[i];
+      }
+      const uint64_t hit = __ballot(my_digit >= 0);
+      const int src = hit ? (int)__builtin_ctzll(hit) : 0;
+      const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(my_digit, src);
+      prefix |= digit << shift;
+      pmask |= 255u << shift;
+      remaining -= (uint32_t)__builtin_amdgcn_readlane((int)my_above, src);
+      if (__builtin_amdgcn_readlane((int)my_exact, src) && prefix != 0u) {   // the whole boundary bin is taken
+        at_or_above = true;
+        break;
+      }
+    }
+    thresh = at_or_above ? prefix - 1u : prefix;
+    take_eq = at_or_above ? 0u : remaining;
+  }
+  // emit in ascending index order, 64 keys per ballot: keys above the
+  // threshold, and the first take_eq keys equal to it
+  if (take_all) {
+    for (int j = lane; j < n; j += kWave) lds_out[j] = j;
+  } else if (kk > 0) {
+    int base = 0;
+    uint32_t eq_seen = 0;
+    for (int j0 = 0; j0 < n; j0 += U * kWave) {
+      uint32_t kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kWave + lane;
+        kv[u] = keys[j < n ? j : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * kWave + lane;
+        const bool eq = j < n && kv[u] == thresh;
+        const uint64_t meq = __ballot(eq);
+        const bool keep = (j < n && kv[u] > thresh) ||
+                          (eq && eq_seen + (uint32_t)__builtin_popcountll(meq & below) < take_eq);
+        const uint64_t mk = __ballot(keep);
+        if (keep) lds_out[base + __builtin_popcountll(mk & below)] = j;
+        base += __builtin_popcountll(mk);
+        eq_seen += (uint32_t)__builtin_popcountll(meq);
+      }
+    }
+  }
+  const int nsel = take_all ? n : kk;
+  for (int m = nsel + lane; m < k_max; m += kWave) lds_out[m] = -1;
+  wave_lds_sync();
+  return nsel;
+}
+
 // |a & b| / |a| for two ascending index lists in LDS (1 when a is empty).
 template <int NT>
 __device__ __forceinline__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb,

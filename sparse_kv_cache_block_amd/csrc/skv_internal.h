@@ -140,17 +140,23 @@ hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hi
 bool step_kernel_available(const skv_problem& p);
 // Static LDS bytes of the step kernel for the problem's K/V type and block size.
 size_t step_static_lds_bytes(const skv_problem& p);
+// Items (32-token slices) one step workgroup can hold: each of its 8 waves
+// keeps one item descriptor per lane.
+constexpr int kStepMaxItems = 8 * 64;
 // LDS of one compute unit on gfx950, the most one workgroup may use.
 constexpr size_t kLdsPerCu = 160 * 1024;
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 // LDS bytes of a scoring workgroup: qbar [T][d] floats, keys [T][score_cols]
-// (fused selection only), the selected ids [2][k_max] and two 256-bin
-// top-byte key histograms.
-__host__ __device__ inline size_t score_lds_bytes(int T, int D, int score_cols, int k_max, bool fused) {
+// (fused selection only), the selected ids [2][k_max], two 256-bin top-byte
+// key histograms and, for the single-launch step, the physical blocks of
+// the candidates [score_cols].
+__host__ __device__ inline size_t score_lds_bytes(int T, int D, int score_cols, int k_max, bool fused,
+                                                  bool table = false) {
   size_t b = (size_t)T * D * 4;
   if (fused) b += (size_t)T * score_cols * 4 + (size_t)2 * k_max * 4 + (size_t)2 * 256 * 4;
+  if (table) b += (size_t)score_cols * 4;
   return b;
 }
 

@@ -144,8 +144,8 @@ Plan make_plan(const skv_problem& p) {
   // single-launch step
   pl.fused_step = 0;
 #ifndef SKV_NO_STEP_KERNEL
-  if (step_kernel_available(p) && pairs >= kStepMinPairs) {
-    pl.step_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true);
+  if (step_kernel_available(p) && pairs >= kStepMinPairs && (p.k_max + nwb) * sub <= kStepMaxItems) {
+    pl.step_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true, true);
     pl.fused_step = pl.step_lds <= kStepMaxScoreLds &&
                     step_static_lds_bytes(p) + pl.step_lds <= kLdsPerCu;
   }

@@ -4,14 +4,16 @@
 // log-sum-exp, in a single launch with one 8-wave workgroup per pair.
 //
 // The window part does not depend on the selection (Beyond abstract: the
-// recent window is attended densely, the older entries sparsely per head), so
-// the workgroup's item list puts the window slices first and each wave issues
-// the loads of its first window slice as soon as its scoring is done: the
-// radix select runs in LDS while those loads are in flight, and its barriers
-// wait for LDS traffic only.  The window descriptors and the attention's query
-// operand are loaded before the scoring; the sparse descriptors (block ids from
-// the selection in LDS, physical ids from the block table) after it, while the
-// waves work through their window slices.
+// recent window is attended densely, the older entries sparsely per head).
+// Once the scores are in LDS, wave t alone runs the radix select of query
+// token t (no workgroup barrier) while the other waves attend the window
+// slices, whose loads they issued as soon as their scoring was done.  Wave 0
+// then raises an LDS flag; a wave that runs out of window slices waits for
+// that flag, then takes selected blocks one at a time from an LDS counter,
+// so the waves that finish the window early take more of them.  The window
+// descriptors, the attention's query operand and the block-table row of the
+// candidates are loaded before the scoring, so the selected blocks' physical
+// ids come from LDS.
 //
 // The selection stays in LDS until the attention is done (global stores
 // issued during the select would queue behind the window loads), and the
@@ -30,6 +32,7 @@ constexpr int kPairThreads = kPairWaves * kWave;
 #ifndef SKV_PAIR_SCORE_UR
 #define SKV_PAIR_SCORE_UR 4
 #endif
+constexpr int kTableRegs = 2;   // block-table entries per thread held through the scoring
 
 // The sequence whose length has rank r in descending order (ties to the lower
 // index).  Every wave computes it (scalar broadcasts of 64 lengths at a time),
@@ -62,6 +65,8 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   extern __shared__ __attribute__((aligned(16))) uint32_t score_smem[];
   __shared__ TopkShared<kPairThreads> sh;
   __shared__ int s_flag;
+  __shared__ int s_sel_ready;
+  __shared__ int s_late_next;
 
   // workgroups start in row order: with more pairs than compute units, rows
   // take the sequences longest first so the short pairs fill in at the end
@@ -76,42 +81,72 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   nsel = max(0, min(nsel, a.k_max));
   const int nwin_items = window_blocks(a, L, ws) * C::SUB;
   const int count = nwin_items + nsel * C::SUB;
-  uint32_t* keys = score_smem + s.T * D;
-  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + s.T * s.score_cols);
-  float overlap = 1.0f;
+  const int T = s.T;
+  const int w = wave_id(), lane = lane_id();
+  // dynamic LDS: group-summed queries, keys [T][score_cols], selected ids
+  // [2][k_max], top-byte key histograms [2][256], the candidates' physical
+  // blocks [score_cols]
+  uint32_t* keys = score_smem + T * D;
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + T * s.score_cols);
+  const uint32_t* hist0 = reinterpret_cast<const uint32_t*>(lds_idx + 2 * s.k_max);
+  int32_t* lds_table = lds_idx + 2 * s.k_max + 2 * 256;
+  if (threadIdx.x == 0) {
+    s_sel_ready = 0;
+    s_late_next = 0;
+  }
+  // the candidates' row of the block table: loaded into registers before the
+  // scoring's loads, stored to LDS after them (no wait in between)
+  const int32_t* table_row = a.block_table + (int64_t)b * a.max_blocks;
+  int32_t trow[kTableRegs];
+#pragma unroll
+  for (int i = 0; i < kTableRegs; ++i) {
+    const int j = (int)threadIdx.x + kPairThreads * i;
+    trow[i] = table_row[j < nc ? j : 0];
+  }
 
-  attend_items<KV, D, BLK, kPairWaves>(
-      a, smem, b, g, 0, count,
-      // window slices first (clamped for lanes past them) ...
+  attend_items<KV, D, BLK, kPairWaves, 1, false, true>(
+      a, smem, b, g, 0, count, nwin_items, T,
+      // window slices, early: taken by the waves that do not select
+      [&](int item) { return describe_window<KV, D, BLK>(a, b, g, item / C::SUB, item % C::SUB, ws); },
+      // selected blocks, late: ids from the selection, physical blocks from
+      // the table row, both in LDS
       [&](int item) {
-        if (nwin_items == 0) return ItemDesc{0, 0, 0};
-        const int it = min(item, nwin_items - 1);
-        return describe_window<KV, D, BLK>(a, b, g, it / C::SUB, it % C::SUB, ws);
-      },
-      // ... then the selected blocks, described once the selection is in LDS
-      [&](int item) {
-        if (nsel == 0) return ItemDesc{0, 0, 0};
-        const int it = max(item - nwin_items, 0);
-        const int m = min(it / C::SUB, nsel - 1);
-        return describe_sparse<KV, D, BLK>(a, b, g, m, lds_idx[m], -1, it % C::SUB);
-      },
-      [&](int item) { return item < nwin_items; },
-      [&](auto&& issue_first) {
-        (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem);
-        issue_first();
+        const int it = item - nwin_items;
+        const int m = it / C::SUB;
+        const int j = lds_idx[m];
+        return describe_paged<KV, D, BLK>(j, lds_table[j], it % C::SUB);
       },
       [&] {
-        // the selection stays in LDS here: global stores would queue behind
-        // the window loads just issued
-        lds_barrier();
-        overlap = select_rows<kPairThreads, false>(nullptr, 0, false, keys, s.score_cols, nc, s.T, k, s.k_max,
-                                                   nullptr, 0, nullptr, 0, nullptr, lds_idx, sh,
-                                                   reinterpret_cast<const uint32_t*>(lds_idx + 2 * s.k_max));
-      });
+        while (__hip_atomic_load(&s_sel_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+          __builtin_amdgcn_s_sleep(1);
+      },
+      [&](auto&& issue_first) {
+        (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem);
+#pragma unroll
+        for (int i = 0; i < kTableRegs; ++i) {
+          const int j = (int)threadIdx.x + kPairThreads * i;
+          if (j < nc) lds_table[j] = trow[i];
+        }
+        for (int j = (int)threadIdx.x + kPairThreads * kTableRegs; j < nc; j += kPairThreads)
+          lds_table[j] = table_row[j];
+        lds_barrier();   // every wave's keys, key histograms and table entries are in LDS
+        issue_first();   // the window slices' waves issue their first slice
+      },
+      [&] {
+        // wave t selects token t's blocks alone while the other waves attend
+        // the window; wave 0 then releases the waves waiting for its ids
+        if (w < T) {
+          (void)wave_select(keys + w * s.score_cols, nc, k, s.k_max, lds_idx + w * s.k_max, sh.hist[w],
+                            hist0 + w * 256);
+          if (w == 0 && lane == 0) __hip_atomic_store(&s_sel_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      },
+      &s_late_next);
   attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag, nullptr);
 
   // ---- the selection's outputs: ids (-1 past the count), counts, overlap
-  const int T = s.T;
+  // (every wave has passed the combine barriers, so both tokens' ids are in LDS)
+  const float overlap = T == 2 ? list_overlap<kPairThreads>(lds_idx, nsel, lds_idx + s.k_max, nsel, sh) : 1.0f;
   for (int i = threadIdx.x; i < T * s.k_max; i += kPairThreads) {
     const int t = i / s.k_max, m = i % s.k_max;
     s.indices[(((int64_t)b * T + t) * s.Hkv + g) * s.k_max + m] = lds_idx[i];
@@ -119,6 +154,8 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   if (threadIdx.x < T) s.n_sel[((int64_t)b * T + threadIdx.x) * s.Hkv + g] = nsel;
   if (T == 2 && s.overlap && threadIdx.x == 0) s.overlap[b * s.Hkv + g] = overlap;
 }
+
+static_assert(kStepMaxItems == kPairWaves * kWave, "one item descriptor per lane");
 
 bool step_kernel_available(const skv_problem& p) {
   return p.pool_location == SKV_POOL_DEVICE && p.head_dim == 128 && p.q_dtype == SKV_BF16 &&

@@ -67,6 +67,9 @@ def test_decode_step_launch_count(lib):
     assert B.sparsekv_decode_step_launches(_good_problem()) == 2
     assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, d=64))) == 2
     assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, blk=16))) == 2
+    # more items per (sequence, KV head) than one workgroup's 8 x 64 descriptors
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, k_max=495))) == 1
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, k_max=496))) == 2
     host = B.make_problem(32, 1, 32, 8, 128, 32, 1024, 32 * 1024, 8 * 32 * 128, 32 * 128, 512, 64,
                           "bf16", "bf16", "bf16", pool_location=B.SKV_POOL_HOST)
     assert B.sparsekv_decode_step_launches(host) == 3

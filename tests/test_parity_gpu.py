@@ -180,6 +180,13 @@ def test_single_launch_bf16(kw, lens):
     check_single_launch(configs.LLAMA32K.scaled(**args), seq_lens=lens)
 
 
+def test_many_blocks_fall_back_to_two_launches():
+    # 600 selected blocks + 17 window blocks exceed one step workgroup's 512 item slots
+    wl = configs.LLAMA32K.scaled(batch=16, context=32768, top_k=600)
+    inp, st = check_step(wl)
+    assert B.sparsekv_decode_step_launches(st.pr) == 2
+
+
 def test_single_launch_longest_first():
     # 40 x 8 = 320 pairs, more than the compute units: the step visits the
     # sequences longest first; every output row must still be its own sequence's
