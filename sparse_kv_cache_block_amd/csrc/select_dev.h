@@ -63,8 +63,10 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
 template <int NT>
 struct TopkShared {
   uint32_t hist[2][256];
+  uint32_t hist1[2][256];   // the second token's, when two tokens select side by side
   uint32_t scan_w[2][NT / kWave];
   uint32_t digit, above, exact, common;
+  uint32_t digit2[2], above2[2], exact2[2];
 };
 
 template <bool PUB>
@@ -198,6 +200,134 @@ __device__ __forceinline__ int block_select(const uint32_t* keys, int n, int k, 
     lds_out[m] = -1;
   }
   lds_barrier();  // scan buffer and lds_out are reused by the caller
+  return nsel;
+}
+
+// The selections of two query tokens made side by side: threads [0, NT/2)
+// count and emit token 0's keys (keys[0..n)), threads [NT/2, NT) token 1's
+// (keys[key_stride..]); the two share every barrier, and each half's result
+// is exactly block_select's for its token.  Token t's ids go to
+// lds_out + t * k_max and, unless out is null, out + t * out_t_stride.
+// Returns k' (the same for both tokens).
+template <int NT, bool PUB>
+__device__ __forceinline__ int block_select_two(const uint32_t* keys, int key_stride, int n, int k, int k_max,
+                                                int32_t* out, int64_t out_t_stride, int32_t* lds_out,
+                                                TopkShared<NT>& sh) {
+  constexpr int NH = NT / 2, NWH = NH / kWave;
+  static_assert(NH >= 256 && NWH >= 2, "a half clears 256 bins and has two waves");
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int half = tid / NH, htid = tid % NH, hw = w % NWH;
+  const uint32_t* kt = keys + half * key_stride;
+  uint32_t(*hist)[256] = half ? sh.hist1 : sh.hist;
+  int kk = k < n ? k : n;
+  if (kk > k_max) kk = k_max;
+  if (kk < 0) kk = 0;
+  const bool take_all = kk >= n;
+  uint32_t thresh = 0, take_eq = 0;
+  if (!take_all && kk > 0) {
+    // both tokens' state in every thread, so the pass loop stays uniform
+    uint32_t prefix[2] = {0, 0}, pmask[2] = {0, 0}, remaining[2] = {(uint32_t)kk, (uint32_t)kk};
+    bool done[2] = {false, false};
+    if (htid < 256) hist[0][htid] = 0;
+    lds_barrier();
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (!done[half])
+        for (int j = htid; j < n; j += NH) {
+          const uint32_t key = kt[j];
+          if ((key & pmask[half]) == prefix[half]) atomicAdd(&hist[pass & 1][(key >> shift) & 255u], 1u);
+        }
+      lds_barrier();
+      if (hw == 0) {
+        if (!done[half]) {
+          uint32_t c[4], lsum = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            c[i] = hist[pass & 1][255 - 4 * lane - i];
+            lsum += c[i];
+          }
+          uint32_t above = wave_inclusive_scan(lsum) - lsum;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (above < remaining[half] && above + c[i] >= remaining[half]) {
+              sh.digit2[half] = 255u - 4 * lane - i;
+              sh.above2[half] = above;
+              sh.exact2[half] = above + c[i] == remaining[half];
+            }
+            above += c[i];
+          }
+        }
+      } else if (hw == 1) {
+        for (int t = lane; t < 256; t += kWave) hist[(pass + 1) & 1][t] = 0;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (done[t]) continue;
+        prefix[t] |= sh.digit2[t] << shift;
+        pmask[t] |= 255u << shift;
+        remaining[t] -= sh.above2[t];
+        if (sh.exact2[t] && prefix[t] != 0u) {   // the whole boundary bin is taken
+          done[t] = true;
+          prefix[t] -= 1u;                     // then every key at or above the old prefix is kept
+          remaining[t] = 0;
+        }
+      }
+      if (done[0] && done[1]) break;
+    }
+    thresh = prefix[half];
+    take_eq = remaining[half];
+  }
+  // emit each token in ascending index order: thread htid of a half owns
+  // indices [j0, j1) of its token
+  const int per = (n + NH - 1) / NH;
+  const int j0 = htid * per;
+  const int j1 = min(n, j0 + per);
+  uint32_t gt = 0, eq = 0;
+  if (!take_all && kk > 0)
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = kt[j];
+      gt += key > thresh;
+      eq += key == thresh;
+    }
+  // exclusive scan within the half: wave scans, then the half's earlier waves
+  const uint32_t v = (gt << 16) | eq;
+  const uint32_t x = wave_inclusive_scan(v);
+  if (lane == kWave - 1) sh.scan_w[0][w] = x;
+  lds_barrier();
+  uint32_t ex = x - v;
+  for (int i = half * NWH; i < w; ++i) ex += sh.scan_w[0][i];
+  int32_t* lo = lds_out + half * k_max;
+  int32_t* go = out ? out + half * out_t_stride : nullptr;
+  if (take_all) {
+    for (int j = j0; j < j1; ++j) {
+      if (go) put_i32<PUB>(go + j, j);
+      lo[j] = j;
+    }
+  } else if (kk > 0) {
+    const uint32_t gt_before = ex >> 16, eq_before = ex & 0xffffu;
+    int pos = (int)(gt_before + min(eq_before, take_eq));
+    uint32_t eq_seen = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = kt[j];
+      bool keep = key > thresh;
+      if (key == thresh) {
+        keep = eq_seen < take_eq;
+        ++eq_seen;
+      }
+      if (keep) {
+        if (go) put_i32<PUB>(go + pos, j);
+        lo[pos] = j;
+        ++pos;
+      }
+    }
+  }
+  const int nsel = take_all ? n : kk;
+  for (int m = nsel + htid; m < k_max; m += NH) {
+    if (go) put_i32<PUB>(go + m, -1);
+    lo[m] = -1;
+  }
+  lds_barrier();
   return nsel;
 }
 
@@ -337,21 +467,28 @@ __device__ __forceinline__ int n_candidates(int L, int window, int blk) {
   return (ws + blk - 1) / blk;
 }
 
-// Keys of one token's row from a score array in global memory into LDS.
+// Keys of every token's row (T <= 2; token t's at row + t * t_stride) from a
+// score array in global memory into LDS (token t's at keys + t * key_stride),
+// both rows in the same round of loads.
 template <int NT>
-__device__ __forceinline__ void load_keys(const float* row, int nc, bool coherent, uint32_t* keys) {
-  constexpr int KB = 8;  // loads in flight per thread
+__device__ __forceinline__ void load_keys(const float* row, int64_t t_stride, int T, int nc, bool coherent,
+                                          uint32_t* keys, int key_stride) {
+  constexpr int KB = 8;  // loads in flight per thread and row
   for (int j0 = threadIdx.x; j0 < nc; j0 += KB * NT) {
-    float v[KB];
+    float v0[KB], v1[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int j = j0 + u * NT;
-      v[u] = j < nc ? (coherent ? fetch_f32(row + j) : row[j]) : 0.f;
+      v0[u] = j < nc ? (coherent ? fetch_f32(row + j) : row[j]) : 0.f;
+      v1[u] = (T == 2 && j < nc) ? (coherent ? fetch_f32(row + t_stride + j) : row[t_stride + j]) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int j = j0 + u * NT;
-      if (j < nc) keys[j] = score_key(v[u]);
+      if (j < nc) {
+        keys[j] = score_key(v0[u]);
+        if (T == 2) keys[key_stride + j] = score_key(v1[u]);
+      }
     }
   }
 }
@@ -371,10 +508,26 @@ __device__ __forceinline__ float select_rows(const float* scores, int64_t t_stri
                                             int32_t* lds_idx, TopkShared<NT>& sh,
                                             const uint32_t* hist0 = nullptr) {
   int ns0 = 0, ns1 = 0;
+  // with a row of keys per token, both are loaded and selected side by side;
+  // with one shared row (key_stride 0) the tokens go one after the other
+  const bool side_by_side = T == 2 && key_stride != 0 && !hist0;
+  if (scores && key_stride != 0) {
+    load_keys<NT>(scores, t_stride, T, nc, coherent, keys, key_stride);
+    lds_barrier();
+  }
+  if (side_by_side) {
+    // the two tokens' selections side by side, one per half of the workgroup
+    const int ns = block_select_two<NT, PUB>(keys, key_stride, nc, k, k_max, indices, idx_t_stride, lds_idx, sh);
+    if (n_sel && threadIdx.x < 2) put_i32<PUB>(n_sel + threadIdx.x * nsel_t_stride, ns);
+    lds_barrier();
+    const float ov = list_overlap<NT>(lds_idx, ns, lds_idx + k_max, ns, sh);
+    if (overlap_out && threadIdx.x == 0) put_f32<PUB>(overlap_out, ov);
+    return ov;
+  }
   for (int t = 0; t < T; ++t) {
     uint32_t* kt = keys + t * key_stride;
-    if (scores) {
-      load_keys<NT>(scores + t * t_stride, nc, coherent, kt);
+    if (scores && key_stride == 0) {
+      load_keys<NT>(scores + t * t_stride, 0, 1, nc, coherent, kt, 0);
       lds_barrier();
     }
     const int ns = block_select<NT, PUB>(kt, nc, k, k_max, indices ? indices + t * idx_t_stride : nullptr,
@@ -587,18 +740,17 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int g, int b
   int32_t* idx_out = p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max;
   int32_t* nsel_out = p.n_sel + (int64_t)b * T * p.Hkv + g;
   float* ov_out = p.overlap ? p.overlap + b * p.Hkv + g : nullptr;
-  if (SINGLE || p.single_chunk) {
+  const bool single = SINGLE || p.single_chunk;
+  if (single) {
     lds_barrier();
-    (void)select_rows<NT, PUB>(nullptr, 0, false, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
-                         (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
   } else {
     // ---- several chunks: the last one of (b, g) to arrive selects
     if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, s_flag)) return false;
-    (void)select_rows<NT, PUB>(sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max, idx_out,
-                         (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
   }
-  if (p.phys)
-    write_phys<NT, PUB>(lds_idx, T, p.k_max, p.block_table + (int64_t)b * p.max_blocks,
+  (void)select_rows<NT, PUB>(single ? nullptr : sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max,
+                             idx_out, (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
+  if (p.phys)   // the attention reads the real token's physical blocks only
+    write_phys<NT, PUB>(lds_idx, 1, p.k_max, p.block_table + (int64_t)b * p.max_blocks,
                         p.phys + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max);
   return true;
 }

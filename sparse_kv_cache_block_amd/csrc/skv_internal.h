@@ -140,9 +140,13 @@ hipError_t launch_step(const ScoreParams& s, const AttnParams& a, size_t lds, hi
 bool step_kernel_available(const skv_problem& p);
 // Static LDS bytes of the step kernel for the problem's K/V type and block size.
 size_t step_static_lds_bytes(const skv_problem& p);
-// Items (32-token slices) one step workgroup can hold: each of its 8 waves
-// keeps one item descriptor per lane.
-constexpr int kStepMaxItems = 8 * 64;
+// Waves of a single-launch step workgroup, and the items (32-token slices)
+// it can hold: each wave keeps one item descriptor per lane.
+#ifndef SKV_PAIR_WAVES
+#define SKV_PAIR_WAVES 8
+#endif
+constexpr int kStepWaves = SKV_PAIR_WAVES;
+constexpr int kStepMaxItems = kStepWaves * 64;
 // LDS of one compute unit on gfx950, the most one workgroup may use.
 constexpr size_t kLdsPerCu = 160 * 1024;
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);

@@ -27,7 +27,7 @@
 
 namespace skv {
 
-constexpr int kPairWaves = 8;
+constexpr int kPairWaves = kStepWaves;
 constexpr int kPairThreads = kPairWaves * kWave;
 #ifndef SKV_PAIR_SCORE_UR
 #define SKV_PAIR_SCORE_UR 4
