@@ -259,6 +259,52 @@ def cobatched_probe(reps: int, instances: int) -> int:
     return 0
 
 
+def hybrid_probe(reps: int) -> int:
+    """Host workload, one layer-step: the hybrid step (selected blocks attended
+    by the host in place, window on the GPU, LSE fusion) against the all-GPU
+    host-pool step (selected blocks gathered over the host link, then attended
+    on the GPU).  Wall time per call, the device synchronised after each batch."""
+    import torch
+
+    from sparse_kv_cache_block_amd import configs
+    from sparse_kv_cache_block_amd.configs import ELEM_BYTES
+    from sparse_kv_cache_block_amd.inputs import make_inputs
+    from sparse_kv_cache_block_amd.step import DecodeStep, HybridHost, to_device_for
+
+    wl = configs.HOST
+    torch.cuda.set_device(0)
+    st = DecodeStep(to_device_for(make_inputs(wl, device="cuda", instance=0)))
+    host = HybridHost(st)
+    for _ in range(3):
+        st.run()
+        st.run_hybrid(host)
+    torch.cuda.synchronize()
+
+    def timed(fn) -> float:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / reps
+
+    t_gpu, t_hyb = [], []
+    for _ in range(3):
+        t_gpu.append(timed(st.run))
+        t_hyb.append(timed(lambda: st.run_hybrid(host)))
+    t_gpu, t_hyb = statistics.median(t_gpu), statistics.median(t_hyb)
+    nsel = int(st.n_sel[:, 0].sum())
+    kv_bytes = nsel * 2 * wl.block_size * wl.head_dim * ELEM_BYTES[wl.kv_dtype]
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    print(json.dumps({
+        "probe": "hybrid_step", "workload": "host (B8, L131072, Hq32/Hkv8, blk64, k32, W512, bf16, pinned pool)",
+        "reps": reps, "gpu_host_path_us": round(t_gpu, 1), "hybrid_us": round(t_hyb, 1),
+        "speedup": round(t_gpu / t_hyb, 3), "selected_kv_bytes": kv_bytes,
+        "gpu_path_link_gbps": round(kv_bytes / (t_gpu * 1e-6) / 1e9, 1),
+        "hybrid_host_gbps": round(kv_bytes / (t_hyb * 1e-6) / 1e9, 1), "host_threads": threads}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +319,8 @@ def main() -> int:
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     ap.add_argument("--gather-correct", action="store_true",
                     help="only compare the full host gather with the speculative correction and exit")
+    ap.add_argument("--hybrid", action="store_true",
+                    help="only compare the hybrid CPU-GPU step with the all-GPU host-pool step and exit")
     ap.add_argument("--cobatched", action="store_true",
                     help="only compare co-batched two-token attention with one launch per token and exit")
     args = ap.parse_args()
@@ -282,6 +330,8 @@ def main() -> int:
         return gather_correct_probe(max(1, min(args.steps, 50)))
     if args.cobatched:
         return cobatched_probe(max(1, args.steps), max(1, args.instances))
+    if args.hybrid:
+        return hybrid_probe(max(1, min(args.steps, 50)))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

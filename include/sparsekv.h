@@ -278,6 +278,46 @@ skv_status sparsekv_decode_step(const skv_problem *pr, const skv_step_inputs *in
                                 void *stream, void *copy_stream);
 
 /*
+ * Host side of the hybrid step: the pool's host addresses and pinned host
+ * buffers the caller owns (allocated with hipHostMalloc or equivalent, so the
+ * GPU can read o and lse).  The call fills the buffers below.
+ */
+typedef struct {
+    const void *k_pool, *v_pool;  /* host addresses of the pinned K/V pool (the memory whose
+                                     device-visible addresses are in skv_step_inputs) */
+    int32_t n_threads;            /* host threads for the sparse part; <= 0: all available */
+    void *q;                      /* [B][T][Hq][d] q_dtype: copy of the queries */
+    int32_t *seq_lens;            /* [B] */
+    int32_t *block_table;         /* [B][max_blocks] */
+    int32_t *indices;             /* [B][T][Hkv][k_max]: copy of the selection */
+    int32_t *n_sel;               /* [B][T][Hkv] */
+    float *k_scales, *v_scales;   /* [P][Hkv]: copies of the fp8 scales (fp8 only) */
+    float *o;                     /* [B][Hq][d]: the sparse part's output */
+    float *lse;                   /* [B][Hq]: its log-sum-exp (natural log) */
+} skv_host_part;
+
+/*
+ * Hybrid CPU-GPU decode step (Beyond abstract: dense attention over the
+ * recent KV in GPU memory, parallel per-head sparse attention over the
+ * salient KV in CPU memory, the outputs fused by log-sum-exp, so that only
+ * small results cross the host link).  Host pool only.
+ *   GPU: scoring and top-k as in sparsekv_decode_step, then attention over
+ *        the window buffers alone;
+ *   CPU: on the calling thread's OpenMP team, the real token's attention over
+ *        its selected blocks, read from the pinned pool in place (fp32
+ *        arithmetic);
+ *   GPU: the two parts fused by log-sum-exp into out->out / out->lse.
+ * The results equal sparsekv_decode_step's up to fp32 rounding.  The call
+ * blocks the calling thread until the selection has reached the host and
+ * the sparse part is done (the window attention runs meanwhile); the fusion
+ * is enqueued on `stream` and runs asynchronously.  fp8 pools need window
+ * 0 (fp8 window buffers are not supported).
+ */
+skv_status sparsekv_decode_step_hybrid(const skv_problem *pr, const skv_step_inputs *in,
+                                       const skv_step_outputs *out, const skv_host_part *host,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Host-pool layer pipeline with a two-slot (ping-pong) staging buffer
  * (DualDecoder Fig. 11 and the layer-aware schedule of its mechanism
  * summary).  Layer l's blocks are gathered into slot l % 2 on copy_stream as

@@ -26,7 +26,7 @@ EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_workspace_size", "sparsekv_workspace_init", "sparsekv_score",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
             "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
-            "sparsekv_attend_cobatched")
+            "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid")
 
 
 class SkvError(RuntimeError):
@@ -62,6 +62,13 @@ class StepOutputs(C.Structure):
                 ("lse", C.c_void_p), ("overlap", C.c_void_p)]
 
 
+class HostPart(C.Structure):
+    _fields_ = [("k_pool", C.c_void_p), ("v_pool", C.c_void_p), ("n_threads", C.c_int32),
+                ("q", C.c_void_p), ("seq_lens", C.c_void_p), ("block_table", C.c_void_p),
+                ("indices", C.c_void_p), ("n_sel", C.c_void_p), ("k_scales", C.c_void_p),
+                ("v_scales", C.c_void_p), ("o", C.c_void_p), ("lse", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -91,6 +98,8 @@ def lib() -> C.CDLL:
                                           vp, vp, vp, vp, sz, vp]),
             "sparsekv_attend_cobatched": (C.c_int, [P, vp, C.POINTER(KvSource), vp, vp,
                                                     C.POINTER(KvSource), vp, vp, vp, vp, sz, vp]),
+            "sparsekv_decode_step_hybrid": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
+                                                      C.POINTER(HostPart), vp, sz, vp]),
             "sparsekv_decode_step": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
                                                vp, vp, vp, vp, vp, sz, vp, vp]),
             "sparsekv_decode_layers": (C.c_int, [P, C.c_int32, C.POINTER(StepInputs),
@@ -231,6 +240,13 @@ def sparsekv_decode_step(pr: Problem, inputs: StepInputs, outputs: StepOutputs, 
                                       _ptr(v_stage), _ptr(k_stage_scales), _ptr(v_stage_scales),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream), cs), "sparsekv_decode_step")
+
+
+def sparsekv_decode_step_hybrid(pr: Problem, inputs: StepInputs, outputs: StepOutputs, host: HostPart,
+                                workspace: torch.Tensor, stream=None) -> None:
+    _check(lib().sparsekv_decode_step_hybrid(C.byref(pr), C.byref(inputs), C.byref(outputs), C.byref(host),
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream(stream)), "sparsekv_decode_step_hybrid")
 
 
 def sparsekv_decode_layers(pr: Problem, inputs: Sequence[StepInputs], outputs: Sequence[StepOutputs],

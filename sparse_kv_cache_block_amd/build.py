@@ -1,4 +1,5 @@
-"""Build libsparsekv.so (gfx950) from csrc/*.hip with hipcc, in-tree."""
+"""Build libsparsekv.so (gfx950) in-tree: csrc/*.hip with hipcc, and the host
+code of the hybrid step (csrc/*.cpp, OpenMP) with the system C++ compiler."""
 from __future__ import annotations
 
 import concurrent.futures as cf
@@ -18,8 +19,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", os.path.join(HERE, "..", "include")]
 
 
+CXX = os.environ.get("CXX_HOST", "g++")
+# x86-64-v3 (AVX2, FMA, F16C): every MI355X host CPU has it
+CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fopenmp", "-march=x86-64-v3", "-Wall"]
+
+
 def sources(src_dir: str = CSRC) -> list[str]:
-    return sorted(glob.glob(os.path.join(src_dir, "*.hip")))
+    return sorted(glob.glob(os.path.join(src_dir, "*.hip")) + glob.glob(os.path.join(src_dir, "*.cpp")))
 
 
 def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD_DIR,
@@ -30,10 +36,13 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str 
 
     def compile_one(src: str) -> str:
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *FLAGS, *extra_flags, "-c", src, "-o", obj]
+        if src.endswith(".cpp"):
+            cmd = [CXX, *CXX_FLAGS, "-c", src, "-o", obj]
+        else:
+            cmd = [HIPCC, *FLAGS, *extra_flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+            raise RuntimeError(f"{cmd[0]} failed for {src}:\n{r.stdout}\n{r.stderr}")
         if verbose and r.stderr.strip():
             print(r.stderr)
         return obj
@@ -41,7 +50,8 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str 
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    # the host code's OpenMP runtime is GCC's (the one the rest of the process uses)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lgomp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = p.seq_lens[b];
   const int ws = L - p.window > 0 ? L - p.window : 0;
-  const int nsel = p.n_sel[(int64_t)b * p.T * p.Hkv + g];
+  const int nsel = p.window_only ? 0 : p.n_sel[(int64_t)b * p.T * p.Hkv + g];
   const int total = (nsel + window_blocks(p, L, ws)) * C::SUB;
   // the pair's items in equal contiguous ranges (at most items_per_split each)
   const int ips = (total + p.n_splits - 1) / p.n_splits;

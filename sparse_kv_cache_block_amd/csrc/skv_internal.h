@@ -78,6 +78,7 @@ struct AttnParams {
   float* lse;               // [B][Hq] or null; co-batched [B][2][Hq]
   int longest_first;        // single-launch step: workgroup row r takes the sequence of
                             // length rank r (descending), so long pairs start first
+  int window_only;          // hybrid step: the sparse part is left to the host
 };
 
 // --------------------------------------------------------------------- gather
@@ -121,7 +122,9 @@ struct Plan {
   // there are enough pairs to fill the chip)
   int fused_step;
   size_t step_lds;          // dynamic LDS bytes of the step kernel (scoring region)
-  size_t off_score_counters, off_attn_counters, off_scores, off_partials, off_phys, total_bytes;
+  size_t off_score_counters, off_attn_counters, off_scores, off_partials, off_phys;
+  size_t off_hybrid;        // hybrid step: the window part's o [B][Hq][d] and lse [B][Hq]
+  size_t total_bytes;
 };
 
 Plan make_plan(const skv_problem& pr);
@@ -150,6 +153,9 @@ constexpr int kStepMaxItems = kStepWaves * 64;
 // LDS of one compute unit on gfx950, the most one workgroup may use.
 constexpr size_t kLdsPerCu = 160 * 1024;
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+// out = log-sum-exp fusion of (o_a, lse_a) (may be null: no part) and (o_b, lse_b), per row of D.
+hipError_t launch_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
+                            float* out, float* lse, int rows, int D, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 // LDS bytes of a scoring workgroup: qbar [T][d] floats, keys [T][score_cols]

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "host_attn.h"
 #include "skv_device.h"
 #include "skv_internal.h"
 
@@ -161,6 +162,8 @@ Plan make_plan(const skv_problem& p) {
   off = align256(off + (size_t)pairs * part_rows * (D + 2) * 4);
   pl.off_phys = off;
   off = align256(off + (size_t)pairs * p.n_q_tokens * p.k_max * 4);
+  pl.off_hybrid = off;
+  off = align256(off + (size_t)p.batch * p.n_q_heads * (D + 1) * 4);
   pl.total_bytes = off;
   return pl;
 }
@@ -649,6 +652,104 @@ skv_status sparsekv_decode_step(const skv_problem* pr, const skv_step_inputs* in
   SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
   return enqueue_host_layer(p, pl, *in, *out, k_stage, v_stage, k_stage_scales, v_stage_scales, ws,
                             s, cs, ev.e[0], ev.e[1], nullptr);
+}
+
+skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inputs* in,
+                                       const skv_step_outputs* out, const skv_host_part* host,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  if (p.pool_location != SKV_POOL_HOST) return fail(SKV_E_UNSUPPORTED, "hybrid step: host pools only");
+  SKV_TRY(check_step_io(p, in, out));
+  if (!host || !host->k_pool || !host->v_pool || !host->q || !host->seq_lens || !host->block_table ||
+      !host->indices || !host->n_sel || !host->o || !host->lse)
+    return fail(SKV_E_NULL, "hybrid step: NULL host buffer");
+  const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
+  if (fp8 && (!host->k_scales || !host->v_scales)) return fail(SKV_E_NULL, "hybrid step: fp8 needs host scales");
+  if (fp8 && p.window > 0) return fail(SKV_E_UNSUPPORTED, "hybrid step: fp8 window buffers");
+  if (p.window > 0 && p.window % p.block_size != 0)
+    return fail(SKV_E_SHAPE, "hybrid step: window buffers need window %% block_size == 0");
+  const Plan pl = make_plan(p);
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = as_stream(stream);
+  const int G = p.n_q_heads / p.n_kv_heads, D = p.head_dim;
+
+  // ---- GPU: scoring and selection, then the inputs of the sparse part to the host
+  SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
+  const size_t qbytes = (size_t)p.batch * p.n_q_tokens * p.n_q_heads * D * elem_bytes(p.q_dtype);
+  const size_t sel = (size_t)p.batch * p.n_q_tokens * p.n_kv_heads;
+  auto d2h = [&](void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, s);
+  };
+  SKV_TRY_HIP(d2h(host->q, in->q, qbytes), "query copy");
+  SKV_TRY_HIP(d2h(host->seq_lens, in->seq_lens, (size_t)p.batch * 4), "length copy");
+  SKV_TRY_HIP(d2h(host->block_table, in->block_table, (size_t)p.batch * p.max_blocks_per_seq * 4), "table copy");
+  SKV_TRY_HIP(d2h(host->indices, out->indices, sel * p.k_max * 4), "selection copy");
+  SKV_TRY_HIP(d2h(host->n_sel, out->n_sel, sel * 4), "selection copy");
+  if (fp8) {
+    SKV_TRY_HIP(d2h(host->k_scales, in->k_scales, (size_t)p.n_pool_blocks * p.n_kv_heads * 4), "scale copy");
+    SKV_TRY_HIP(d2h(host->v_scales, in->v_scales, (size_t)p.n_pool_blocks * p.n_kv_heads * 4), "scale copy");
+  }
+  EventSet ev;
+  SKV_TRY_HIP(ev.make(1), "event create");
+  SKV_TRY_HIP(hipEventRecord(ev.e[0], s), "event record");
+
+  // ---- GPU: attention over the window alone, while the host works
+  float* o_win = reinterpret_cast<float*>(ws + pl.off_hybrid);
+  float* lse_win = o_win + (size_t)p.batch * p.n_q_heads * D;
+  if (p.window > 0) {
+    AttnParams a = attn_params(p, pl, in->q, in->seq_lens, o_win, lse_win, ws);
+    skv_kv_source win{SKV_SRC_WINDOW, in->window_k, in->window_v, nullptr, nullptr, nullptr};
+    SKV_TRY(set_source(p, a, &win, false));
+    // no sparse item is attended; waves without an item read row 0 of the window buffers
+    skv_kv_source none{SKV_SRC_STAGED, in->window_k, in->window_v, nullptr, nullptr, nullptr};
+    SKV_TRY(set_source(p, a, &none, true));
+    a.indices = out->indices;
+    a.n_sel = out->n_sel;
+    a.window_only = 1;
+    SKV_TRY_HIP(launch_attend(a, s), "window attention launch");
+  }
+
+  // ---- host: the sparse part, once the selection has arrived
+  SKV_TRY_HIP(hipEventSynchronize(ev.e[0]), "selection wait");
+  HostAttnArgs h{};
+  h.B = p.batch;
+  h.T = p.n_q_tokens;
+  h.Hq = p.n_q_heads;
+  h.Hkv = p.n_kv_heads;
+  h.D = D;
+  h.blk = p.block_size;
+  h.window = p.window;
+  h.max_blocks = p.max_blocks_per_seq;
+  h.k_max = p.k_max;
+  h.kv_dtype = p.kv_dtype;
+  h.stride_block = p.pool_stride_block;
+  h.stride_head = p.pool_stride_head;
+  h.q = host->q;
+  h.seq_lens = host->seq_lens;
+  h.block_table = host->block_table;
+  h.indices = host->indices;
+  h.n_sel = host->n_sel;
+  h.k_pool = host->k_pool;
+  h.v_pool = host->v_pool;
+  h.k_scales = host->k_scales;
+  h.v_scales = host->v_scales;
+  h.o = host->o;
+  h.lse = host->lse;
+  h.n_threads = host->n_threads;
+  (void)G;
+  host_sparse_attention(h);
+
+  // ---- GPU: fuse the two parts
+  float* o_host = nullptr;
+  float* lse_host = nullptr;
+  SKV_TRY_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&o_host), host->o, 0), "host output address");
+  SKV_TRY_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&lse_host), host->lse, 0), "host lse address");
+  SKV_TRY_HIP(launch_lse_merge(p.window > 0 ? o_win : nullptr, p.window > 0 ? lse_win : nullptr, o_host, lse_host,
+                               out->out, out->lse, p.batch * p.n_q_heads, D, s),
+              "fusion launch");
+  return SKV_OK;
 }
 
 skv_status sparsekv_decode_layers(const skv_problem* pr, int32_t n_layers, const skv_step_inputs* in,

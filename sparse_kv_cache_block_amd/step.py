@@ -79,6 +79,10 @@ class DecodeStep:
                 self._layer_bufs.append(bufs)
         return self._layer_bufs
 
+    def run_hybrid(self, host: "HybridHost", stream=None) -> None:
+        """Host pool: the hybrid step (window on the GPU, selected blocks on the host)."""
+        B.sparsekv_decode_step_hybrid(self.pr, self.inputs, self.outputs, host.part, self.ws, stream)
+
     def run_layers(self, n_layers: int, stream=None, copy_stream=None) -> list:
         """Host pool: n_layers layer-steps over the same inputs through the
         two-slot staging pipeline; returns the per-layer output buffers."""
@@ -110,6 +114,38 @@ class PinnedPool:
 
     def data_ptr(self) -> int:
         return self.dptr
+
+
+class HybridHost:
+    """Pinned host buffers of the hybrid step for one input set (allocation only)."""
+
+    def __init__(self, st: "DecodeStep", n_threads: int = 0):
+        inp, pr = st.inp, st.pr
+        wl = inp.wl
+        if not isinstance(inp.k_pool, PinnedPool):
+            raise ValueError("the hybrid step reads a pinned host pool")
+        Bn, T, Hq, Hkv, d = wl.batch, wl.n_q_tokens, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+
+        def pinned(shape, dtype):
+            return torch.empty(shape, dtype=dtype, pin_memory=True)
+
+        self.q = pinned(tuple(inp.q.shape), inp.q.dtype)
+        self.seq_lens = pinned((Bn,), torch.int32)
+        self.block_table = pinned((Bn, wl.max_blocks), torch.int32)
+        self.indices = pinned((Bn, T, Hkv, pr.k_max), torch.int32)
+        self.n_sel = pinned((Bn, T, Hkv), torch.int32)
+        self.k_scales = self.v_scales = None
+        if inp.k_scales is not None:
+            self.k_scales = pinned(tuple(inp.k_scales.shape), torch.float32)
+            self.v_scales = pinned(tuple(inp.v_scales.shape), torch.float32)
+        self.o = pinned((Bn, Hq, d), torch.float32)
+        self.lse = pinned((Bn, Hq), torch.float32)
+        self.part = B.HostPart(inp.k_pool.tensor.data_ptr(), inp.v_pool.tensor.data_ptr(), int(n_threads),
+                               self.q.data_ptr(), self.seq_lens.data_ptr(), self.block_table.data_ptr(),
+                               self.indices.data_ptr(), self.n_sel.data_ptr(),
+                               self.k_scales.data_ptr() if self.k_scales is not None else None,
+                               self.v_scales.data_ptr() if self.v_scales is not None else None,
+                               self.o.data_ptr(), self.lse.data_ptr())
 
 
 def to_device_for(inp: DecodeInputs, device="cuda") -> DecodeInputs:

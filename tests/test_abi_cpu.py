@@ -181,3 +181,31 @@ def test_workspace_covers_cobatched_partials(lib):
     one = B.sparsekv_workspace_size(_good_problem(T=1, Hq=16, Hkv=2))
     two = B.sparsekv_workspace_size(_good_problem(T=2, Hq=16, Hkv=2))
     assert two > one
+
+
+def test_hybrid_step_validation(lib):
+    # every check runs on the host, before any GPU call
+    d = 0x1000
+    ins = B.StepInputs(d, d, d, d, d, d, d, d, d, d, d)
+    outs = B.StepOutputs(d, d, d, d, None)
+    host = B.HostPart(d, d, 0, d, d, d, d, d, None, None, d, d)
+    dev = _good_problem()
+    n = B.sparsekv_workspace_size(dev)
+    assert lib.sparsekv_decode_step_hybrid(C.byref(dev), C.byref(ins), C.byref(outs), C.byref(host), d, n,
+                                           None) == B.SKV_E_UNSUPPORTED
+    hp = B.make_problem(2, 1, 8, 2, 128, 32, 64, 128, 2 * 32 * 128, 32 * 128, 64, 8, "bf16", "bf16", "bf16",
+                        pool_location=B.SKV_POOL_HOST)
+    n = B.sparsekv_workspace_size(hp)
+    assert lib.sparsekv_decode_step_hybrid(C.byref(hp), C.byref(ins), C.byref(outs), None, d, n,
+                                           None) == B.SKV_E_NULL
+    no_o = B.HostPart(d, d, 0, d, d, d, d, d, None, None, None, d)
+    assert lib.sparsekv_decode_step_hybrid(C.byref(hp), C.byref(ins), C.byref(outs), C.byref(no_o), d, n,
+                                           None) == B.SKV_E_NULL
+    fp8 = B.make_problem(2, 1, 8, 2, 128, 32, 64, 128, 2 * 32 * 128, 32 * 128, 64, 8, "bf16", "fp8", "bf16",
+                         pool_location=B.SKV_POOL_HOST)
+    host8 = B.HostPart(d, d, 0, d, d, d, d, d, d, d, d, d)
+    assert lib.sparsekv_decode_step_hybrid(C.byref(fp8), C.byref(ins), C.byref(outs), C.byref(host8), d,
+                                           B.sparsekv_workspace_size(fp8), None) == B.SKV_E_UNSUPPORTED
+    assert "fp8 window" in B.sparsekv_last_error()
+    assert lib.sparsekv_decode_step_hybrid(C.byref(hp), C.byref(ins), C.byref(outs), C.byref(host), d, 16,
+                                           None) == B.SKV_E_WORKSPACE

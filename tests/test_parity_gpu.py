@@ -450,6 +450,47 @@ def test_speculative_gather_correction(wl):
             assert torch.equal(spare[0][b, g, :n0], ref[0][b, g, :n0])
 
 
+# ------------------------------------------------ hybrid CPU-GPU step
+def check_hybrid(wl, seq_lens=None, n_threads=0):
+    announce(f"decode_step_hybrid {wl.name} B={wl.batch} L={wl.context} kv={wl.kv_dtype} T={wl.n_q_tokens} "
+             f"W={wl.window} seq_lens={seq_lens} threads={n_threads}")
+    from sparse_kv_cache_block_amd.step import HybridHost
+    inp, st = run_step(wl, seq_lens=seq_lens)   # the GPU host-pool step: gather, then attention
+    ref_out, ref_lse, ref_idx = st.out.clone(), st.lse.clone(), st.indices.clone()
+    host = HybridHost(st, n_threads)
+    st.out.fill_(float("nan"))
+    st.lse.fill_(float("nan"))
+    st.run_hybrid(host)
+    torch.cuda.synchronize()
+    assert torch.equal(st.indices, ref_idx)
+    # the same values as the all-GPU step (fp32 rounding apart) ...
+    fin = torch.isfinite(ref_lse)
+    assert torch.equal(fin, torch.isfinite(st.lse))
+    assert bool(torch.all(st.lse[~fin] == -float("inf")))
+    assert (st.out - ref_out).abs().max().item() <= 1e-4
+    if fin.any():
+        assert (st.lse[fin] - ref_lse[fin]).abs().max().item() <= 1e-4
+    # ... and as the oracle on the same selection
+    h = HostArrays(inp)
+    err = compare_attention(inp, h, _np(st.indices), _np(st.n_sel), _np(st.out), _np(st.lse), TOL[wl.kv_dtype])
+    print(f"[case] ok: max-abs err {err:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("wl,lens,threads", [
+    (configs.HOST.scaled(batch=2, context=8192), None, 0),
+    (configs.HOST.scaled(batch=3, context=8192, top_k=40), [8192, 700, 0], 3),
+    (configs.HOST.scaled(batch=2, context=4096, window=0), None, 0),
+    (configs.HOST.scaled(batch=2, context=4096, window=0, kv_dtype="fp8"), None, 0),
+    (configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3), None, 0),
+])
+def test_hybrid_step(wl, lens, threads):
+    check_hybrid(wl, seq_lens=lens, n_threads=threads)
+
+
+def test_hybrid_step_full_host_workload():
+    check_hybrid(configs.HOST)
+
+
 def test_host_layer_pipeline_matches_single_steps():
     wl = configs.HOST.scaled(batch=2, context=8192)
     announce("sparsekv_decode_layers (ping-pong, 4 layers) vs single steps")
