@@ -482,6 +482,10 @@ def check_hybrid(wl, seq_lens=None, n_threads=0):
     (configs.HOST.scaled(batch=2, context=4096, window=0), None, 0),
     (configs.HOST.scaled(batch=2, context=4096, window=0, kv_dtype="fp8"), None, 0),
     (configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3), None, 0),
+    (configs.HOST.scaled(batch=2, context=4096, head_dim=64, block_size=32, n_q_heads=64), None, 2),
+    (configs.HOST.scaled(batch=2, context=4096, n_q_heads=24, top_k=60), None, 0),       # G = 3, k > candidates
+    (configs.HOST.scaled(batch=1, context=2048, kv_dtype="fp32", q_dtype="fp32", landmark_dtype="fp32",
+                         block_size=16, window=64), None, 0),
 ])
 def test_hybrid_step(wl, lens, threads):
     check_hybrid(wl, seq_lens=lens, n_threads=threads)
