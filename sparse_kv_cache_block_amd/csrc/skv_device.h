@@ -81,7 +81,8 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 
 // 16-byte load of streamed, read-once data (K/V chunks, landmarks) with the
-// non-temporal hint, so it does not displace reused lines in the caches.
+// non-temporal hint, so it does not displace reused lines in the caches
+// (plain loads measured 65.6 -> 73.6 us on the 32k step).
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
