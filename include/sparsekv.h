@@ -151,10 +151,12 @@ skv_status sparsekv_workspace_size(const skv_problem *pr, size_t *bytes);
  * Kernel launches one sparsekv_decode_step enqueues for a problem (host-only,
  * no GPU work): 1 when the whole step runs as a single launch with one
  * workgroup per (sequence, KV head) -- device pool, head_dim 128, bf16
- * queries and landmarks, bf16 or fp8 K/V, blocks of 32 or 64 tokens and at
- * least 128 (sequence, KV head) pairs; 2 for the other device-pool problems
- * (scoring with the selection, then attention); 3 for a host pool (scoring
- * with the selection, gather, attention).  *launches receives the count.
+ * queries and landmarks, bf16 or fp8 K/V, blocks of 32 or 64 tokens, at
+ * least 128 (sequence, KV head) pairs, and at most 512 32-token slices per
+ * pair, counted as (k_max + ceil(W / blk) + 1) * blk / 32 (e.g. k_max <= 495
+ * at blocks of 32 and W = 512); 2 for the other device-pool problems (scoring with the
+ * selection, then attention); 3 for a host pool (scoring with the
+ * selection, gather, attention).  *launches receives the count.
  */
 skv_status sparsekv_decode_step_launches(const skv_problem *pr, int32_t *launches);
 skv_status sparsekv_workspace_init(void *workspace, size_t bytes, void *stream);
