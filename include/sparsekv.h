@@ -299,6 +299,20 @@ typedef struct {
 } skv_host_part;
 
 /*
+ * The host part of the hybrid step on its own (Beyond abstract: parallel
+ * per-head sparse attention over the salient KV in CPU memory): for the
+ * real token (t = 0) of every query head h of group g, attention over the
+ * positions p = j*blk + r of the selected blocks j with p < ws_b, from
+ * host->k_pool / v_pool (host addresses), with host->q, seq_lens,
+ * block_table, indices, n_sel (and, for fp8, k_scales / v_scales) already
+ * filled by the caller.  Writes host->o (normalised, fp32) and host->lse
+ * (natural log; -inf and o = 0 when a head has no position).  Runs on the
+ * calling thread's OpenMP team (host->n_threads); no GPU work, blocking.
+ * Needs a host pool problem (pool_location HOST); layouts as above.
+ */
+skv_status sparsekv_host_attention(const skv_problem *pr, const skv_host_part *host);
+
+/*
  * Hybrid CPU-GPU decode step (Beyond abstract: dense attention over the
  * recent KV in GPU memory, parallel per-head sparse attention over the
  * salient KV in CPU memory, the outputs fused by log-sum-exp, so that only

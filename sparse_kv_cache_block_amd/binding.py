@@ -26,7 +26,7 @@ EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_workspace_size", "sparsekv_workspace_init", "sparsekv_score",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
             "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
-            "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid")
+            "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid", "sparsekv_host_attention")
 
 
 class SkvError(RuntimeError):
@@ -100,6 +100,7 @@ def lib() -> C.CDLL:
                                                     C.POINTER(KvSource), vp, vp, vp, vp, sz, vp]),
             "sparsekv_decode_step_hybrid": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
                                                       C.POINTER(HostPart), vp, sz, vp]),
+            "sparsekv_host_attention": (C.c_int, [P, C.POINTER(HostPart)]),
             "sparsekv_decode_step": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
                                                vp, vp, vp, vp, vp, sz, vp, vp]),
             "sparsekv_decode_layers": (C.c_int, [P, C.c_int32, C.POINTER(StepInputs),
@@ -247,6 +248,10 @@ def sparsekv_decode_step_hybrid(pr: Problem, inputs: StepInputs, outputs: StepOu
     _check(lib().sparsekv_decode_step_hybrid(C.byref(pr), C.byref(inputs), C.byref(outputs), C.byref(host),
                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                                              _stream(stream)), "sparsekv_decode_step_hybrid")
+
+
+def sparsekv_host_attention(pr: Problem, host: HostPart) -> None:
+    _check(lib().sparsekv_host_attention(C.byref(pr), C.byref(host)), "sparsekv_host_attention")
 
 
 def sparsekv_decode_layers(pr: Problem, inputs: Sequence[StepInputs], outputs: Sequence[StepOutputs],

@@ -654,6 +654,54 @@ skv_status sparsekv_decode_step(const skv_problem* pr, const skv_step_inputs* in
                             s, cs, ev.e[0], ev.e[1], nullptr);
 }
 
+namespace {
+HostAttnArgs host_args(const skv_problem& p, const skv_host_part& host) {
+  HostAttnArgs h{};
+  h.B = p.batch;
+  h.T = p.n_q_tokens;
+  h.Hq = p.n_q_heads;
+  h.Hkv = p.n_kv_heads;
+  h.D = p.head_dim;
+  h.blk = p.block_size;
+  h.window = p.window;
+  h.max_blocks = p.max_blocks_per_seq;
+  h.k_max = p.k_max;
+  h.kv_dtype = p.kv_dtype;
+  h.stride_block = p.pool_stride_block;
+  h.stride_head = p.pool_stride_head;
+  h.q = host.q;
+  h.seq_lens = host.seq_lens;
+  h.block_table = host.block_table;
+  h.indices = host.indices;
+  h.n_sel = host.n_sel;
+  h.k_pool = host.k_pool;
+  h.v_pool = host.v_pool;
+  h.k_scales = host.k_scales;
+  h.v_scales = host.v_scales;
+  h.o = host.o;
+  h.lse = host.lse;
+  h.n_threads = host.n_threads;
+  return h;
+}
+
+skv_status check_host_part(const skv_problem& p, const skv_host_part* host) {
+  if (p.pool_location != SKV_POOL_HOST) return fail(SKV_E_UNSUPPORTED, "host attention: host pools only");
+  if (!host || !host->k_pool || !host->v_pool || !host->q || !host->seq_lens || !host->block_table ||
+      !host->indices || !host->n_sel || !host->o || !host->lse)
+    return fail(SKV_E_NULL, "host attention: NULL host buffer");
+  if (p.kv_dtype == SKV_FP8_E4M3FN && (!host->k_scales || !host->v_scales))
+    return fail(SKV_E_NULL, "host attention: fp8 needs host scales");
+  return SKV_OK;
+}
+}  // namespace
+
+skv_status sparsekv_host_attention(const skv_problem* pr, const skv_host_part* host) {
+  SKV_TRY(check_problem(pr));
+  SKV_TRY(check_host_part(*pr, host));
+  host_sparse_attention(host_args(*pr, *host));
+  return SKV_OK;
+}
+
 skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inputs* in,
                                        const skv_step_outputs* out, const skv_host_part* host,
                                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -661,11 +709,8 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
   const skv_problem& p = *pr;
   if (p.pool_location != SKV_POOL_HOST) return fail(SKV_E_UNSUPPORTED, "hybrid step: host pools only");
   SKV_TRY(check_step_io(p, in, out));
-  if (!host || !host->k_pool || !host->v_pool || !host->q || !host->seq_lens || !host->block_table ||
-      !host->indices || !host->n_sel || !host->o || !host->lse)
-    return fail(SKV_E_NULL, "hybrid step: NULL host buffer");
+  SKV_TRY(check_host_part(p, host));
   const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
-  if (fp8 && (!host->k_scales || !host->v_scales)) return fail(SKV_E_NULL, "hybrid step: fp8 needs host scales");
   if (fp8 && p.window > 0) return fail(SKV_E_UNSUPPORTED, "hybrid step: fp8 window buffers");
   if (p.window > 0 && p.window % p.block_size != 0)
     return fail(SKV_E_SHAPE, "hybrid step: window buffers need window %% block_size == 0");
@@ -673,7 +718,7 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);
-  const int G = p.n_q_heads / p.n_kv_heads, D = p.head_dim;
+  const int D = p.head_dim;
 
   // ---- GPU: scoring and selection, then the inputs of the sparse part to the host
   SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
@@ -713,33 +758,7 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
 
   // ---- host: the sparse part, once the selection has arrived
   SKV_TRY_HIP(hipEventSynchronize(ev.e[0]), "selection wait");
-  HostAttnArgs h{};
-  h.B = p.batch;
-  h.T = p.n_q_tokens;
-  h.Hq = p.n_q_heads;
-  h.Hkv = p.n_kv_heads;
-  h.D = D;
-  h.blk = p.block_size;
-  h.window = p.window;
-  h.max_blocks = p.max_blocks_per_seq;
-  h.k_max = p.k_max;
-  h.kv_dtype = p.kv_dtype;
-  h.stride_block = p.pool_stride_block;
-  h.stride_head = p.pool_stride_head;
-  h.q = host->q;
-  h.seq_lens = host->seq_lens;
-  h.block_table = host->block_table;
-  h.indices = host->indices;
-  h.n_sel = host->n_sel;
-  h.k_pool = host->k_pool;
-  h.v_pool = host->v_pool;
-  h.k_scales = host->k_scales;
-  h.v_scales = host->v_scales;
-  h.o = host->o;
-  h.lse = host->lse;
-  h.n_threads = host->n_threads;
-  (void)G;
-  host_sparse_attention(h);
+  host_sparse_attention(host_args(p, *host));
 
   // ---- GPU: fuse the two parts
   float* o_host = nullptr;
