@@ -147,11 +147,12 @@ __device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws)
 // One NW-wave workgroup's attention of (b, g) over items [first, first+count)
 // of its list.  The first n_early items are early: described by desc_early
 // before the hooks and taken in turn by waves early_wave0 .. NW-1.  The rest
-// are late: taken in turn by all NW waves (with DYN_LATE: taken one at a
-// time, by whichever wave needs one next, from the LDS counter *late_next,
-// which starts at 0) and described by desc_late, in a wave only once
-// late_ready() has returned in it (late_ready waits until late descriptors
-// can be formed).  A wave works through its early items, then its late ones;
+// are late, shared out by LATE: kLateStrided, in turn over all NW waves;
+// kLateShared, one at a time to whichever wave needs one next, from the LDS
+// counter *late_next (which starts at 0; the split then depends on timing,
+// so fp32 sums vary in their last bits from run to run).  Late items are
+// described by desc_late, in a wave only once late_ready() has returned in
+// it (late_ready waits until late descriptors can be formed).  A wave works through its early items, then its late ones;
 // lane j of the wave holds the descriptor of the wave's j-th item, so a wave
 // takes at most 64 statically assigned items.  The descriptor functions are
 // called for the lanes past a wave's items with its last item of that kind,
@@ -163,7 +164,9 @@ __device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws)
 // such a wave issues nothing and reaches post() at once.  post() runs after
 // pre (both hooks run in every thread).  Leaves each wave's unnormalised O rows, running max
 // and sum in its LDS combine region.
-template <int KV, int D, int BLK, int NW, int NTOK = 1, bool PAD_FIRST = true, bool DYN_LATE = false,
+constexpr int kLateStrided = 0, kLateShared = 1;
+
+template <int KV, int D, int BLK, int NW, int NTOK = 1, bool PAD_FIRST = true, int LATE = kLateStrided,
           class EarlyDescFn, class LateDescFn, class LateReadyFn, class PreFn, class PostFn>
 __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, int b, int g, int first,
                                              int count, int n_early, int early_wave0, EarlyDescFn desc_early,
@@ -209,12 +212,13 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   }
 
   // this wave's items: early ones strided over waves early_wave0 .. NW-1,
-  // then late ones strided over every wave
+  // then its late ones
+  constexpr bool DYN_LATE = LATE == kLateShared;
   const int ew = NW - early_wave0, we = w - early_wave0;
   const int n_late = count - n_early;
   const int my_early = (we >= 0 && n_early > we) ? (n_early - we + ew - 1) / ew : 0;
   const int my_late = DYN_LATE ? 0 : (n_late > w ? (n_late - w + NW - 1) / NW : 0);
-  int my_items = my_early + my_late;   // with DYN_LATE it grows as late items are taken
+  int my_items = my_early + my_late;   // with kLateShared it grows as late items are taken
   // lane j describes this wave's item j; early and late descriptors stay in
   // separate registers, so reading an early item never waits for the loads
   // behind a late one

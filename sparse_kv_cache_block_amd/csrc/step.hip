@@ -8,9 +8,8 @@
 // Once the scores are in LDS, wave t alone runs the radix select of query
 // token t (no workgroup barrier) while the other waves attend the window
 // slices, whose loads they issued as soon as their scoring was done.  Wave 0
-// then raises an LDS flag; a wave that runs out of window slices waits for
-// that flag, then takes selected blocks one at a time from an LDS counter,
-// so the waves that finish the window early take more of them.  The window
+// then raises an LDS flag; a wave that reaches its first selected block
+// waits for that flag.  The window
 // descriptors, the attention's query operand and the block-table row of the
 // candidates are loaded before the scoring, so the selected blocks' physical
 // ids come from LDS.
@@ -33,6 +32,12 @@ constexpr int kPairThreads = kPairWaves * kWave;
 #define SKV_PAIR_SCORE_UR 4
 #endif
 constexpr int kTableRegs = 2;   // block-table entries per thread held through the scoring
+// Selected blocks go to the waves in turn, so a pair's result is the same on
+// every run.  Handing them out from an LDS counter instead (kLateShared)
+// measured 0.5 us faster at llama32k but makes the fp32 sums depend on timing.
+#ifndef SKV_STEP_LATE
+#define SKV_STEP_LATE kLateStrided
+#endif
 
 // The sequence whose length has rank r in descending order (ties to the lower
 // index).  Every wave computes it (scalar broadcasts of 64 lengths at a time),
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
     trow[i] = table_row[j < nc ? j : 0];
   }
 
-  attend_items<KV, D, BLK, kPairWaves, 1, false, true>(
+  attend_items<KV, D, BLK, kPairWaves, 1, false, SKV_STEP_LATE>(
       a, smem, b, g, 0, count, nwin_items, T,
       // window slices, early: taken by the waves that do not select
       [&](int item) { return describe_window<KV, D, BLK>(a, b, g, item / C::SUB, item % C::SUB, ws); },

@@ -539,6 +539,37 @@ def test_alternating_inputs_share_one_workspace():
                 assert torch.equal(st.out, out) and torch.equal(st.lse, lse)
 
 
+# ------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("wl", [configs.LLAMA32K.scaled(batch=16, context=4096),          # one launch
+                                configs.DUAL.scaled(batch=2, context=8192, top_k=30)])     # two launches
+def test_graph_replays_match_eager(wl):
+    # the step enqueues no memset and its kernels return their counters to
+    # zero, so a captured step replays exactly; eager work runs between replays
+    announce(f"graph capture of decode_step {wl.name} B={wl.batch} L={wl.context}")
+    inp, st = run_step(wl)
+    ref = (st.out.clone(), st.lse.clone(), st.indices.clone(), st.n_sel.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st.run()
+    for _ in range(3):
+        st.out.fill_(float("nan"))
+        st.lse.fill_(float("nan"))
+        st.indices.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (st.out, st.lse, st.indices, st.n_sel)
+        assert all(torch.equal(a, b) for a, b in zip(got, ref))
+        st.run()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(got, ref))
+
+
 # ------------------------------------------------------------ full-size workloads
 @pytest.mark.parametrize("name", ["llama32k", "dual", "ragged", "host"])
 def test_full_size_workload(name):
