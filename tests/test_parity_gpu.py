@@ -570,6 +570,26 @@ def test_graph_replays_match_eager(wl):
         assert all(torch.equal(a, b) for a, b in zip(got, ref))
 
 
+def test_concurrent_streams_keep_results():
+    # the library keeps no state outside the caller's workspace: two steps with
+    # their own workspaces, enqueued on two streams at once, give each one's
+    # stand-alone result (one single-launch, one two-launch shape)
+    announce("two decode steps on two streams at once")
+    _, a = run_step(configs.LLAMA32K.scaled(batch=16, context=4096))
+    _, b = run_step(configs.DUAL.scaled(batch=2, context=8192, top_k=30))
+    ref = [(st.out.clone(), st.indices.clone()) for st in (a, b)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for _ in range(5):
+        for st in (a, b):
+            st.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for st, sm in zip((a, b), streams):
+            st.run(stream=sm.cuda_stream)
+        torch.cuda.synchronize()
+        for st, (o, i) in zip((a, b), ref):
+            assert torch.equal(st.out, o) and torch.equal(st.indices, i)
+
+
 # ------------------------------------------------------------ full-size workloads
 @pytest.mark.parametrize("name", ["llama32k", "dual", "ragged", "host"])
 def test_full_size_workload(name):
