@@ -1,7 +1,8 @@
 // step.hip -- the whole decode step of one (sequence, KV head) in one
 // workgroup, for gfx950: landmark scoring into LDS, the per-head top-k, and
 // the attention over the recent window and the selected blocks, fused by
-// log-sum-exp, in a single launch with one 8-wave workgroup per pair.
+// log-sum-exp, in a single launch with one workgroup of kStepWaves (8)
+// waves per pair.
 //
 // The window part does not depend on the selection (Beyond abstract: the
 // recent window is attended densely, the older entries sparsely per head).
@@ -9,10 +10,9 @@
 // token t (no workgroup barrier) while the other waves attend the window
 // slices, whose loads they issued as soon as their scoring was done.  Wave 0
 // then raises an LDS flag; a wave that reaches its first selected block
-// waits for that flag.  The window
-// descriptors, the attention's query operand and the block-table row of the
-// candidates are loaded before the scoring, so the selected blocks' physical
-// ids come from LDS.
+// waits for that flag.  The window descriptors, the attention's query
+// operand and the block-table row of the candidates are loaded before the
+// scoring, so the selected blocks' physical ids come from LDS.
 //
 // The selection stays in LDS until the attention is done (global stores
 // issued during the select would queue behind the window loads), and the
