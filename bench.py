@@ -57,13 +57,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks or empty lines."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def kernel_source_digest(kernel: str) -> str:
-    """sha256 over a kernel's sources (counter results go stale when they change)."""
+    """sha256 over a kernel's sources, comments aside (counter results go stale
+    when the code changes)."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "sparse_kv_cache_block_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_kv_cache_block_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
