@@ -506,6 +506,30 @@ def test_host_layer_pipeline_matches_single_steps():
         assert torch.equal(o["out"], st.out) and torch.equal(o["lse"], st.lse)
 
 
+def test_host_pipeline_depth_and_delayed_copy_stream():
+    # two slots for any depth: 2 and 8 layers give the single step's result; and
+    # with the copy stream held up by a long kernel, every layer's attention
+    # still waits for its own gather (the events order them)
+    wl = configs.HOST.scaled(batch=2, context=8192)
+    announce("host ping-pong pipeline: 2 and 8 layers, delayed copy stream")
+    inp, st = run_step(wl)
+    ref = (st.out.clone(), st.lse.clone(), st.indices.clone())
+    for n in (2, 8):
+        outs = st.run_layers(n, copy_stream=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        assert len(outs) == n
+        for o in outs:
+            assert torch.equal(o["indices"], ref[2])
+            assert torch.equal(o["out"], ref[0]) and torch.equal(o["lse"], ref[1])
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        torch.cuda._sleep(200_000_000)   # a bounded spin kernel, tens of ms
+    outs = st.run_layers(4, copy_stream=cs)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o["out"], ref[0]) and torch.equal(o["lse"], ref[1])
+
+
 def test_repeated_calls_reuse_workspace():
     wl = configs.LLAMA32K.scaled(batch=2, context=4096)
     announce("repeated decode steps on one workspace")
