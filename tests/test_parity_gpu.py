@@ -439,6 +439,31 @@ def test_speculative_gather_correction(wl):
             if fp8:
                 assert np.array_equal(_np(out[2])[b, g, :n0], okss[b, g, :n0])
                 assert np.array_equal(_np(out[3])[b, g, :n0], ovss[b, g, :n0])
+    # a wrong prediction: every real id moved up by one (inside the candidates),
+    # so hits fall at arbitrary slots and most blocks are misses
+    L = _np(dev.seq_lens)
+    bad = np.full_like(idx, -1)
+    bad_n = np.zeros_like(nsel)
+    for b in range(Bn):
+        nc = -(-max(0, int(L[b]) - wl.window) // wl.block_size)
+        for g in range(Hkv):
+            ids = sorted({int(j) + 1 for j in idx[b, 0, g, :int(nsel[b, 0, g])] if int(j) + 1 < nc})
+            bad[b, 0, g, :len(ids)] = ids
+            bad_n[b, 0, g] = len(ids)
+    bad_t, bad_nt = torch.from_numpy(bad).cuda(), torch.from_numpy(bad_n).cuda()
+    wrong = stage()
+    B.sparsekv_gather(pr, *pools, bad_t, bad_nt, *wrong)
+    fixed = stage()
+    B.sparsekv_gather_correct(pr, *pools, bad_t, bad_nt, 0, *wrong, st.indices, st.n_sel, 0, *fixed, misses=miss)
+    torch.cuda.synchronize()
+    for b in range(Bn):
+        for g in range(Hkv):
+            n0 = int(nsel[b, 0, g])
+            hits = len(set(idx[b, 0, g, :n0].tolist()) & set(bad[b, 0, g, :int(bad_n[b, 0, g])].tolist()))
+            assert int(miss[b, g]) == n0 - hits
+            for a, r in zip(fixed, ref):
+                if a is not None:
+                    assert torch.equal(a[b, g, :n0], r[b, g, :n0])
     # identical selections: nothing is missed, the stage is moved as it is
     B.sparsekv_gather_correct(pr, *pools, st.indices, st.n_sel, 0, *ref, st.indices, st.n_sel, 0, *spare,
                               misses=miss)
