@@ -65,6 +65,7 @@ struct TopkShared {
   uint32_t hist[2][256];
   uint32_t hist1[2][256];   // the second token's, when two tokens select side by side
   uint32_t scan_w[2][NT / kWave];
+  uint32_t ov_w[NT / kWave];          // list_overlap's per-wave hit counts
   uint32_t digit, above, exact, common;
   uint32_t digit2[2], above2[2], exact2[2];
 };
@@ -441,25 +442,38 @@ __device__ __forceinline__ int wave_select(const uint32_t* keys, int n, int k, i
   return nsel;
 }
 
-// |a & b| / |a| for two ascending index lists in LDS (1 when a is empty).
+// |a & b| / |a| for two lists of distinct ids in [0, n_ids) in LDS (1 when a
+// is empty).  b's ids are marked in an LDS bitmap (`bits`, ceil(n_ids / 32)
+// words of scratch), a's ids test it, and the hits are summed with ballots:
+// three LDS round trips, no search and no shared counter.
 template <int NT>
-__device__ __forceinline__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb,
-                                              TopkShared<NT>& sh) {
-  if (threadIdx.x == 0) sh.common = 0;
+__device__ __forceinline__ float list_overlap(const int32_t* a, int na, const int32_t* b, int nb, int n_ids,
+                                              uint32_t* bits, TopkShared<NT>& sh) {
+  constexpr int NW = NT / kWave;
+  const int words = (n_ids + 31) / 32;
+  for (int i = threadIdx.x; i < words; i += NT) bits[i] = 0u;
   lds_barrier();
-  uint32_t local = 0;
-  for (int i = threadIdx.x; i < na; i += NT) {
-    const int x = a[i];
-    int lo = 0, hi = nb;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (b[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    local += (lo < nb && b[lo] == x) ? 1u : 0u;
+  for (int i = threadIdx.x; i < nb; i += NT) {
+    const uint32_t x = (uint32_t)b[i];
+    atomicOr(&bits[x >> 5], 1u << (x & 31u));
   }
-  if (local) atomicAdd(&sh.common, local);
   lds_barrier();
-  return na > 0 ? (float)sh.common / (float)na : 1.0f;
+  uint32_t hits = 0;
+  for (int i0 = 0; i0 < na; i0 += NT) {
+    const int i = i0 + (int)threadIdx.x;
+    bool hit = false;
+    if (i < na) {
+      const uint32_t x = (uint32_t)a[i];
+      hit = (bits[x >> 5] >> (x & 31u)) & 1u;
+    }
+    hits += (uint32_t)__builtin_popcountll(__ballot(hit));
+  }
+  if (lane_id() == 0) sh.ov_w[wave_id()] = hits;
+  lds_barrier();
+  uint32_t common = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) common += sh.ov_w[w];
+  return na > 0 ? (float)common / (float)na : 1.0f;
 }
 
 __device__ __forceinline__ int n_candidates(int L, int window, int blk) {
@@ -520,7 +534,7 @@ __device__ __forceinline__ float select_rows(const float* scores, int64_t t_stri
     const int ns = block_select_two<NT, PUB>(keys, key_stride, nc, k, k_max, indices, idx_t_stride, lds_idx, sh);
     if (n_sel && threadIdx.x < 2) put_i32<PUB>(n_sel + threadIdx.x * nsel_t_stride, ns);
     lds_barrier();
-    const float ov = list_overlap<NT>(lds_idx, ns, lds_idx + k_max, ns, sh);
+    const float ov = list_overlap<NT>(lds_idx, ns, lds_idx + k_max, ns, nc, keys, sh);
     if (overlap_out && threadIdx.x == 0) put_f32<PUB>(overlap_out, ov);
     return ov;
   }
@@ -538,10 +552,20 @@ __device__ __forceinline__ float select_rows(const float* scores, int64_t t_stri
   }
   float ov = 1.0f;
   if (T == 2) {
-    ov = list_overlap<NT>(lds_idx, ns0, lds_idx + k_max, ns1, sh);
+    ov = list_overlap<NT>(lds_idx, ns0, lds_idx + k_max, ns1, nc, keys, sh);
     if (overlap_out && threadIdx.x == 0) put_f32<PUB>(overlap_out, ov);
   }
   return ov;
+}
+
+// The selection of every token (T <= 2) over keys already in LDS (token t's
+// at keys + t * key_stride): positions, ascending, to lds_idx + t * k_max
+// (-1 past k'), nothing to global memory.  Returns k'.
+template <int NT>
+__device__ __forceinline__ int select_lds(const uint32_t* keys, int key_stride, int n, int T, int k, int k_max,
+                                          int32_t* lds_idx, TopkShared<NT>& sh) {
+  if (T == 2) return block_select_two<NT, false>(keys, key_stride, n, k, k_max, nullptr, 0, lds_idx, sh);
+  return block_select<NT, false>(keys, n, k, k_max, nullptr, lds_idx, sh);
 }
 
 // Physical block of every selected index (row b of the block table).
@@ -588,7 +612,8 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
     row_begin = c * R;
     row_end = min(p.max_blocks, row_begin + R);
   }
-  const bool in_lds = LDS_KEYS || (p.fused_select && p.single_chunk);
+  // fused: the keys stay in LDS when this workgroup selects over them
+  const bool in_lds = LDS_KEYS || (p.fused_select && (p.single_chunk || p.two_level));
 
   float* qbar = reinterpret_cast<float*>(smem);  // [T][D]
   uint32_t* keys = smem + T * D;                 // [T][score_cols]
@@ -729,26 +754,104 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
 // nc: the candidates of sequence b, k: its k (both as read by the caller).
 // SINGLE: compiled for the single-chunk mode only.
 template <int NT, bool PUB, bool SINGLE = false>
-__device__ __forceinline__ bool select_scored(const ScoreParams& p, int g, int b, int nc, int k,
+__device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g, int b, int nc, int k,
                                               uint32_t* smem, TopkShared<NT>& sh, int* s_flag) {
   const int T = p.T;
-  const int nchunks = max(1, (nc + p.rows_per_chunk - 1) / p.rows_per_chunk);
+  const int R = p.rows_per_chunk;
+  const int nchunks = max(1, (nc + R - 1) / R);
   uint32_t* keys = smem + T * p.D;
   int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + T * p.score_cols);
-  float* sc = p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
-  const int64_t t_stride = (int64_t)p.Hkv * p.score_cols;
   int32_t* idx_out = p.indices + ((int64_t)b * T * p.Hkv + g) * p.k_max;
   int32_t* nsel_out = p.n_sel + (int64_t)b * T * p.Hkv + g;
   float* ov_out = p.overlap ? p.overlap + b * p.Hkv + g : nullptr;
   const bool single = SINGLE || p.single_chunk;
-  if (single) {
-    lds_barrier();
+  if (single || !p.two_level) {
+    // one chunk: the keys are in LDS; several: the last chunk of (b, g) to
+    // arrive reads every published score
+    if (single) {
+      lds_barrier();
+    } else if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, s_flag)) {
+      return false;
+    }
+    const float* sc = single ? nullptr : p.scores + ((int64_t)b * T * p.Hkv + g) * p.score_cols;
+    (void)select_rows<NT, PUB>(sc, (int64_t)p.Hkv * p.score_cols, true, keys, p.score_cols, nc, T, k, p.k_max,
+                               idx_out, (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
   } else {
-    // ---- several chunks: the last one of (b, g) to arrive selects
+    // ---- several chunks.  Level 1: the chunk keeps its own top-k' and
+    // publishes it as (key, id).  Under the selection's total order (key
+    // descending, id ascending) a block among the pair's top k' is among its
+    // chunk's top k', so these candidates hold the whole selection.
+    const int k_max = p.k_max;
+    const int row_begin = c * R;
+    const int rows = min(nc, row_begin + R) - row_begin;
+    int32_t* cand = p.cand + ((int64_t)b * T * p.Hkv + g) * p.cand_stride;
+    const int64_t cand_t = (int64_t)p.Hkv * p.cand_stride;
+    lds_barrier();   // the chunk's keys are in LDS
+    const int ns1 = select_lds<NT>(keys + row_begin, p.score_cols, rows, T, k, k_max, lds_idx, sh);
+    for (int i = threadIdx.x; i < T * ns1; i += NT) {
+      const int t = i / ns1, m = i - t * ns1;
+      const int pos = lds_idx[t * k_max + m];
+      int32_t* ct = cand + t * cand_t + (int64_t)c * 2 * k_max;
+      put_i32<true>(ct + m, (int32_t)keys[t * p.score_cols + row_begin + pos]);
+      put_i32<true>(ct + k_max + m, row_begin + pos);
+    }
     if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, s_flag)) return false;
+    // Level 2, in the last chunk to arrive: every chunk's candidates in chunk
+    // order, so position order is id order and ties still go to the lowest id.
+    int kk = k < k_max ? k : k_max;
+    if (kk < 0) kk = 0;
+    const int m_full = min(kk, R);                        // candidates of a full chunk
+    const int m_last = min(kk, nc - (nchunks - 1) * R);   // of the last chunk
+    const int M = (nchunks - 1) * m_full + m_last;
+    // Candidate j of a token is slot j - cc * m_full of chunk cc.
+    int32_t* ids = reinterpret_cast<int32_t*>(lds_idx + 2 * k_max + 2 * 256);   // [T][score_cols]
+    const bool ids_lds = p.cand_ids_lds != 0;
+    constexpr int KB = 4;   // candidates per thread whose loads are in flight together
+    for (int i0 = threadIdx.x; i0 < T * M; i0 += KB * NT) {
+      int32_t kv[KB], iv[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int i = i0 + u * NT;
+        const int t = i / M, j = i - t * M;
+        const int cc = min(j / max(m_full, 1), nchunks - 1);
+        const int32_t* ct = cand + t * cand_t + (int64_t)cc * 2 * k_max + (j - cc * m_full);
+        kv[u] = i < T * M ? fetch_i32(ct) : 0;
+        iv[u] = (ids_lds && i < T * M) ? fetch_i32(ct + k_max) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int i = i0 + u * NT;
+        if (i < T * M) {
+          const int t = i / M, j = i - t * M;
+          keys[t * p.score_cols + j] = (uint32_t)kv[u];
+          if (ids_lds) ids[t * p.score_cols + j] = iv[u];
+        }
+      }
+    }
+    lds_barrier();
+    const int ns = select_lds<NT>(keys, p.score_cols, M, T, k, k_max, lds_idx, sh);
+    for (int i = threadIdx.x; i < T * k_max; i += NT) {
+      const int t = i / k_max, m = i - t * k_max;
+      const int pos = lds_idx[i];
+      int32_t id = -1;
+      if (pos >= 0) {
+        if (ids_lds) {
+          id = ids[t * p.score_cols + pos];
+        } else {   // the ids did not fit in LDS: read the selected ones back
+          const int cc = min(pos / max(m_full, 1), nchunks - 1);
+          id = fetch_i32(cand + t * cand_t + (int64_t)cc * 2 * k_max + k_max + (pos - cc * m_full));
+        }
+      }
+      lds_idx[i] = id;
+      put_i32<PUB>(idx_out + t * (int64_t)p.Hkv * k_max + m, id);
+    }
+    if (threadIdx.x < T) put_i32<PUB>(nsel_out + threadIdx.x * p.Hkv, ns);
+    lds_barrier();
+    if (T == 2) {
+      const float ov = list_overlap<NT>(lds_idx, ns, lds_idx + k_max, ns, nc, keys, sh);
+      if (ov_out && threadIdx.x == 0) put_f32<PUB>(ov_out, ov);
+    }
   }
-  (void)select_rows<NT, PUB>(single ? nullptr : sc, t_stride, true, keys, p.score_cols, nc, T, k, p.k_max,
-                             idx_out, (int64_t)p.Hkv * p.k_max, nsel_out, p.Hkv, ov_out, lds_idx, sh);
   if (p.phys)   // the attention reads the real token's physical blocks only
     write_phys<NT, PUB>(lds_idx, 1, p.k_max, p.block_table + (int64_t)b * p.max_blocks,
                         p.phys + ((int64_t)b * T * p.Hkv + g) * p.k_max, (int64_t)p.Hkv * p.k_max);
@@ -762,7 +865,7 @@ __device__ __forceinline__ bool score_task(const ScoreParams& p, int c, int g, i
                                            TopkShared<NT>& sh, int* s_flag) {
   if (!score_rows<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, smem)) return false;
   if (!p.fused_select) return false;
-  return select_scored<NT, PUB>(p, g, b, n_candidates(p.seq_lens[b], p.window, p.blk), p.k_per_seq[b],
+  return select_scored<NT, PUB>(p, c, g, b, n_candidates(p.seq_lens[b], p.window, p.blk), p.k_per_seq[b],
                                 smem, sh, s_flag);
 }
 

@@ -31,6 +31,13 @@ struct ScoreParams {
   unsigned* counters;       // [B][Hkv], zero between calls
   const int32_t* block_table;  // when set, the selection also writes
   int32_t* phys;               // phys[b][t][g][m] = block_table[b][indices[b][t][g][m]]
+  // fused, several chunks, two_level: each chunk's own top-k as (key, id)
+  // rows, [B][T][Hkv][chunks][2][k_max] (cand_stride = chunks * 2 * k_max);
+  // otherwise the chunks publish every score to `scores`
+  int two_level;
+  int32_t* cand;
+  int cand_stride;
+  int cand_ids_lds;         // 1: the last chunk stages the candidates' ids in LDS (when they fit)
 };
 
 struct TopkParams {
@@ -115,6 +122,7 @@ struct GatherParams {
 struct Plan {
   int max_cand;             // upper bound of candidates per sequence
   int rows_per_chunk, score_chunks;
+  int score_two_level;      // several chunks: select per chunk, then over the chunks' candidates
   int items_per_split, n_splits;   // attention split-K
   int cob_items_per_split, cob_n_splits;   // co-batched two-token attention (T = 2)
   // single-launch step: one workgroup per (sequence, KV head) scores,
@@ -162,13 +170,23 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 // (fused selection only), the selected ids [2][k_max], two 256-bin top-byte
 // key histograms and, for the single-launch step, the physical blocks of
 // the candidates [score_cols].
+// Layout: group-summed queries [T][D] fp32, keys [T][score_cols], selected
+// ids [2][k_max], top-byte histograms [2][256]; then the step kernel's
+// block-table row [score_cols] (table) or, for a fused selection over several
+// chunks, the candidates' ids [T][score_cols] (cand_ids).
 __host__ __device__ inline size_t score_lds_bytes(int T, int D, int score_cols, int k_max, bool fused,
-                                                  bool table = false) {
+                                                  bool table = false, bool cand_ids = false) {
   size_t b = (size_t)T * D * 4;
   if (fused) b += (size_t)T * score_cols * 4 + (size_t)2 * k_max * 4 + (size_t)2 * 256 * 4;
   if (table) b += (size_t)score_cols * 4;
+  if (cand_ids) b += (size_t)T * score_cols * 4;
   return b;
 }
+
+// LDS of one workgroup (bytes), and an allowance for the score kernel's
+// static LDS (selection state) next to its dynamic region.
+constexpr size_t kLdsPerWorkgroup = 160 * 1024;
+constexpr size_t kScoreStaticLds = 8 * 1024;
 
 // LDS bytes the score kernel needs for a fused selection over max_cand keys.
 size_t topk_lds_bytes(int max_cand);

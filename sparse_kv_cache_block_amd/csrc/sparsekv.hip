@@ -90,6 +90,7 @@ int round_up(int x, int m) { return (x + m - 1) / m * m; }
 constexpr int kAttnTargetWorkgroups = SKV_ATTN_TARGET_WGS;   // one 8-wave workgroup per CU
 constexpr int kScoreSinglePairs = 128;       // from this many pairs on, one scoring workgroup per pair
 constexpr int kScoreTargetWorkgroups = 256;
+constexpr int kTwoLevelMinSaving = 2048;     // keys the chunks' own selections must save
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // single-launch step: used from this many (sequence, KV head) pairs on (one
@@ -119,6 +120,12 @@ Plan make_plan(const skv_problem& p) {
     pl.rows_per_chunk = round_up((pl.max_cand + per_pair - 1) / per_pair, rps);
   }
   pl.score_chunks = pl.max_cand > 0 ? (pl.max_cand + pl.rows_per_chunk - 1) / pl.rows_per_chunk : 1;
+  // Selecting within each chunk first costs a second select (measured about
+  // 3.3 us fixed plus 2 us per 1000 keys per token) and a hand-off of about
+  // 1.5 us; it pays when it leaves the last chunk at least 2048 fewer keys.
+  pl.score_two_level = pl.score_chunks > 1 &&
+                       pl.max_cand - pl.rows_per_chunk - pl.score_chunks * std::min(p.k_max, pl.rows_per_chunk) >=
+                           kTwoLevelMinSaving;
   // attention: items (32-token slices) of the sparse + window list per split,
   // aiming at about three resident workgroups per compute unit
   const int sub = blk / attn_item_tokens(kv_kind(p.kv_dtype), blk);
@@ -157,7 +164,10 @@ Plan make_plan(const skv_problem& p) {
   pl.off_attn_counters = off;
   off = align256(off + (size_t)pairs * 4);
   pl.off_scores = off;
-  off = align256(off + (size_t)pairs * p.n_q_tokens * (pl.max_cand > 0 ? pl.max_cand : 1) * 4);
+  // stand-alone scores, or a fused selection's per-chunk (key, id) candidates
+  const size_t score_words = (size_t)(pl.max_cand > 0 ? pl.max_cand : 1);
+  const size_t cand_words = pl.score_two_level ? (size_t)pl.score_chunks * 2 * p.k_max : 0;
+  off = align256(off + (size_t)pairs * p.n_q_tokens * std::max(score_words, cand_words) * 4);
   pl.off_partials = off;
   off = align256(off + (size_t)pairs * part_rows * (D + 2) * 4);
   pl.off_phys = off;
@@ -273,6 +283,11 @@ skv_status enqueue_score_select(const skv_problem& p, const Plan& pl, const skv_
   sp.rows_per_chunk = pl.rows_per_chunk;
   sp.fused_select = 1;
   sp.single_chunk = pl.score_chunks == 1;
+  sp.two_level = pl.score_two_level;
+  sp.cand = reinterpret_cast<int32_t*>(ws + pl.off_scores);
+  sp.cand_stride = pl.score_chunks * 2 * p.k_max;
+  sp.cand_ids_lds = score_lds_bytes(sp.T, sp.D, sp.score_cols, sp.k_max, true, false, true) + kScoreStaticLds <=
+                    kLdsPerWorkgroup;
   sp.block_table = in.block_table;
   sp.phys = reinterpret_cast<int32_t*>(ws + pl.off_phys);
   sp.k_per_seq = in.k_per_seq;

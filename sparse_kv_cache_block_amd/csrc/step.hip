@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
 
   // ---- the selection's outputs: ids (-1 past the count), counts, overlap
   // (every wave has passed the combine barriers, so both tokens' ids are in LDS)
-  const float overlap = T == 2 ? list_overlap<kPairThreads>(lds_idx, nsel, lds_idx + s.k_max, nsel, sh) : 1.0f;
+  const float overlap = T == 2 ? list_overlap<kPairThreads>(lds_idx, nsel, lds_idx + s.k_max, nsel, nc, keys, sh) : 1.0f;
   for (int i = threadIdx.x; i < T * s.k_max; i += kPairThreads) {
     const int t = i / s.k_max, m = i % s.k_max;
     s.indices[(((int64_t)b * T + t) * s.Hkv + g) * s.k_max + m] = lds_idx[i];

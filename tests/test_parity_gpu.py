@@ -155,6 +155,37 @@ def test_dual_identical_tokens_overlap_one():
     assert np.all(_np(st.overlap) == 1.0)
 
 
+def test_two_tokens_many_candidates_few_pairs():
+    """Two tokens, 2 (sequence, KV head) pairs and 9996 candidates each: the
+    scoring rows are split over many workgroups, and the selecting workgroup's
+    candidate ids (2 x 9996 words) do not fit in its LDS next to the keys, so
+    the selected ids are read back from the workspace."""
+    wl = configs.DUAL.scaled(batch=1, n_q_heads=16, n_kv_heads=2, block_size=16, context=160000,
+                             window=64, top_k=64)
+    check_step(wl, gen_device="cuda")
+
+
+# 2 sequences x 2 KV heads, 4080 candidates, k 16: each of 64 scoring workgroups
+# per pair keeps its own top 16 (1024 candidates) and the last one selects
+TWO_LEVEL = configs.LLAMA32K.scaled(batch=2, n_q_heads=8, n_kv_heads=2, context=131072, top_k=16)
+
+
+@pytest.mark.parametrize("wl", [TWO_LEVEL, TWO_LEVEL.scaled(n_q_tokens=2, spec_noise=0.3)],
+                         ids=["one_token", "two_tokens"])
+def test_two_level_selection_ragged(wl):
+    """Chunk counts differ per sequence: the second has 1221 candidates, 19 full
+    chunks of 64 and a last one of 5 rows, which keeps fewer than k."""
+    check_step(wl, seq_lens=[131072, 39584], gen_device="cuda")
+
+
+def test_two_level_selection_ties_go_to_lowest_ids():
+    def zero_q(inp):
+        inp.q.zero_()
+    inp, st = check_step(TWO_LEVEL.scaled(n_q_tokens=2), mutate=zero_q, gen_device="cuda")
+    gi = _np(st.indices)
+    assert np.all(gi == np.arange(16)[None, None, None, :])
+
+
 # ------------------------------------------------ single-launch step (>= 128 pairs)
 # 16 sequences x 8 KV heads: decode_step runs as one launch, one workgroup per pair
 MIXED16 = [4096, 1000, 513, 37, 0, 1, 512, 513, 4000, 2048, 3333, 4095, 64, 700, 2500, 4096]
