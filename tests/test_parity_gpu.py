@@ -230,6 +230,23 @@ def test_single_launch_ragged_poisoned():
     check_single_launch(configs.RAGGED.scaled(batch=16, context=8192, ragged_min=100))
 
 
+# 64 sequences x 8 KV heads = 512 pairs, twice the compute units: two rounds
+# of step workgroups, longest sequences first
+LENS64 = [int(x) for x in np.random.default_rng(11).integers(0, 3073, size=64)]
+LENS64[:6] = [0, 1, 256, 257, 3072, 3072]
+
+
+@pytest.mark.parametrize("wl", [
+    configs.RAGGED.scaled(batch=64, context=3072, ragged_min=0),
+    configs.LLAMA32K.scaled(batch=64, context=3072, top_k=24),
+    configs.LLAMA32K.scaled(batch=64, context=3072, top_k=24, block_size=64, window=0),
+    configs.DUAL.scaled(batch=64, context=3072, window=256, top_k=20),
+], ids=["ragged_poisoned", "bf16", "bf16_blk64_no_window", "dual_fp8"])
+def test_single_launch_two_rounds_of_pairs(wl):
+    lens = None if wl.name == "ragged" else LENS64
+    check_single_launch(wl, seq_lens=lens)
+
+
 @pytest.mark.parametrize("kw", [dict(), dict(block_size=32, context=4096, window=256, top_k=20)])
 def test_single_launch_dual_fp8(kw):
     args = dict(batch=16, context=8192, top_k=30)
