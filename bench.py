@@ -11,8 +11,9 @@ blocks can be served from the 256 MB last-level cache between steps.
 Prints one JSON line: tokens/s (real query tokens per second), the dominant
 kernel's roofline (algorithmic HBM bytes per launch over its mean launch time
 from HIP events on the launch stream: the single-launch step kernel where the
-step is one launch, else the attention launch timed alone), and the CPU oracle
-timed on a bounded sample of the same workload.
+step is one launch, else the attention launch timed alone), that rate against
+the streaming-read ceiling of a plain read with the same loads on the same box,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -102,6 +103,28 @@ def copy_probe(mib: int, reps: int) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps}))
     return 0
+
+
+def read_ceiling_gbps(gib: int = 2, reps: int = 20) -> float:
+    """Streaming-read rate of sparsekv_stream_read (the kernels' own 16-byte
+    non-temporal loads) over a buffer far larger than the last-level cache."""
+    import torch
+    from sparse_kv_cache_block_amd import binding as B
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        B.sparsekv_stream_read(buf, sink)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        B.sparsekv_stream_read(buf, sink)
+    e1.record(stream)
+    e1.synchronize()
+    rate = buf.numel() * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return rate
 
 
 def h2d_ceiling_gbps(mib: int = 64, reps: int = 20) -> float:
@@ -444,6 +467,8 @@ def main() -> int:
 
     roofline = None
     if kernel:
+        ceiling = read_ceiling_gbps()
+        log(f"streaming-read ceiling: {ceiling:.0f} GB/s")
         achieved = k_bytes / (k_ms * 1e-3) / 1e9
         rec = recorded_traffic(kernel, wl.name)
         traffic = None
@@ -452,7 +477,9 @@ def main() -> int:
         roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "bytes_per_launch": int(k_bytes),
-                    "us_per_launch": round(k_ms * 1e3, 2)}
+                    "us_per_launch": round(k_ms * 1e3, 2),
+                    "read_ceiling_gbps": round(ceiling, 1),
+                    "frac_of_read_ceiling": round(achieved / ceiling, 4)}
 
     # ---- CPU oracle on a bounded sample of instance 0
     cpu = None

@@ -137,6 +137,21 @@ const char *sparsekv_last_error(void);
 const char *sparsekv_version(void);
 
 /*
+ * Measurement aid, not a step of the method: reads `bytes` of device memory
+ * at `buffer` once with the same 16-byte non-temporal loads the step's
+ * kernels use, four per thread in flight, so that the rate it reaches on a
+ * buffer far larger than the caches is the streaming-read ceiling the step's
+ * achieved bandwidth can be compared with.  `buffer` and `bytes` must be
+ * multiples of 16 (else SKV_E_SHAPE).  `sink` is a device buffer of
+ * `sink_bytes` (at least 4, 4-aligned); it bounds the grid at one workgroup
+ * per word (16 KiB read per workgroup when there are enough words) and is
+ * written only if a workgroup's folded data equals one fixed 32-bit value, so
+ * its contents carry no meaning.  Asynchronous on `stream`; allocates nothing.
+ */
+skv_status sparsekv_stream_read(const void *buffer, size_t bytes, void *sink, size_t sink_bytes,
+                                void *stream);
+
+/*
  * Workspace: device scratch for split partials, score staging and arrival
  * counters.  sparsekv_workspace_size() gives the bytes needed by
  * sparsekv_attend / sparsekv_decode_step / sparsekv_decode_layers for a

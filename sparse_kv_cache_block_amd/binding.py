@@ -26,7 +26,8 @@ EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_workspace_size", "sparsekv_workspace_init", "sparsekv_score",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
             "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
-            "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid", "sparsekv_host_attention")
+            "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid", "sparsekv_host_attention",
+            "sparsekv_stream_read")
 
 
 class SkvError(RuntimeError):
@@ -88,6 +89,7 @@ def lib() -> C.CDLL:
             "sparsekv_version": (C.c_char_p, []),
             "sparsekv_workspace_size": (C.c_int, [P, C.POINTER(sz)]),
             "sparsekv_workspace_init": (C.c_int, [vp, sz, vp]),
+            "sparsekv_stream_read": (C.c_int, [vp, sz, vp, sz, vp]),
             "sparsekv_score": (C.c_int, [P, vp, vp, vp, vp, vp]),
             "sparsekv_topk": (C.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
             "sparsekv_gather": (C.c_int, [P] + [vp] * 12),
@@ -166,6 +168,12 @@ def sparsekv_decode_step_launches(pr: Problem) -> int:
 def sparsekv_workspace_init(workspace: torch.Tensor, stream=None) -> None:
     _check(lib().sparsekv_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                          _stream(stream)), "sparsekv_workspace_init")
+
+
+def sparsekv_stream_read(buffer: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    _check(lib().sparsekv_stream_read(_ptr(buffer), buffer.numel() * buffer.element_size(), _ptr(sink),
+                                      sink.numel() * sink.element_size(), _stream(stream)),
+           "sparsekv_stream_read")
 
 
 def sparsekv_score(pr: Problem, q, landmarks, seq_lens, scores, stream=None) -> None:

@@ -483,6 +483,19 @@ skv_status sparsekv_workspace_init(void* workspace, size_t bytes, void* stream) 
   return SKV_OK;
 }
 
+skv_status sparsekv_stream_read(const void* buffer, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  if (!buffer || !sink) return fail(SKV_E_NULL, "stream_read: NULL argument");
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buffer) % 16 != 0)
+    return fail(SKV_E_SHAPE, "stream_read: buffer and size must be multiples of 16 bytes");
+  if (sink_bytes < 4 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return fail(SKV_E_SHAPE, "stream_read: the sink needs at least one aligned 32-bit word");
+  const size_t words = sink_bytes / 4;
+  SKV_TRY_HIP(launch_stream_read(buffer, bytes, static_cast<uint32_t*>(sink),
+                                 (int)(words < (1u << 20) ? words : (1u << 20)), as_stream(stream)),
+              "stream read launch");
+  return SKV_OK;
+}
+
 skv_status sparsekv_score(const skv_problem* pr, const void* q, const void* landmarks,
                           const int32_t* seq_lens, float* scores, void* stream) {
   SKV_TRY(check_problem(pr));

@@ -209,3 +209,14 @@ def test_hybrid_step_validation(lib):
     assert "fp8 window" in B.sparsekv_last_error()
     assert lib.sparsekv_decode_step_hybrid(C.byref(hp), C.byref(ins), C.byref(outs), C.byref(host), d, 16,
                                            None) == B.SKV_E_WORKSPACE
+
+
+def test_stream_read_validates_before_launch(lib):
+    vp = C.c_void_p
+    lib.sparsekv_stream_read.argtypes = [vp, C.c_size_t, vp, C.c_size_t, vp]
+    assert lib.sparsekv_stream_read(None, 16, 0x1000, 4, None) == B.SKV_E_NULL
+    assert lib.sparsekv_stream_read(0x1000, 16, None, 4, None) == B.SKV_E_NULL
+    assert lib.sparsekv_stream_read(0x1000, 15, 0x1000, 4, None) == B.SKV_E_SHAPE
+    assert lib.sparsekv_stream_read(0x1008, 16, 0x1000, 4, None) == B.SKV_E_SHAPE
+    assert lib.sparsekv_stream_read(0x1000, 16, 0x1000, 2, None) == B.SKV_E_SHAPE
+    assert len(B.sparsekv_last_error()) > 0

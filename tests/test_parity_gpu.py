@@ -688,6 +688,17 @@ def test_concurrent_streams_keep_results():
 
 
 # ------------------------------------------------------------ full-size workloads
+def test_stream_read_writes_nothing():
+    """The read-ceiling probe reads a buffer (a ragged size: several grid
+    strides plus a tail) and leaves its sink untouched."""
+    announce("stream_read 3 MiB + 48 B")
+    buf = torch.ones((3 << 20) + 48, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    B.sparsekv_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum().item()) == 0
+
+
 @pytest.mark.parametrize("name", ["llama32k", "dual", "ragged", "host"])
 def test_full_size_workload(name):
     wl = configs.get(name)
