@@ -105,6 +105,17 @@ def copy_probe(mib: int, reps: int) -> int:
     return 0
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def read_ceiling_gbps(gib: int = 2, reps: int = 20) -> float:
     """Streaming-read rate of sparsekv_stream_read (the kernels' own 16-byte
     non-temporal loads) over a buffer far larger than the last-level cache."""
@@ -499,11 +510,23 @@ def main() -> int:
             if len(times) >= 50 or (len(times) >= 3 and spent > args.cpu_budget):
                 break
         t = statistics.median(times)
-        cpu = {"value": round(wl.batch / t, 2), "unit": "tokens/s", "cores": O.max_threads(),
+        threads = O.max_threads()
+        # the same steps on one thread (3, about the multi-thread sample's cost again)
+        O.set_threads(1)
+        t1 = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
+            t1.append(time.perf_counter() - t0)
+        O.set_threads(threads)
+        t1 = statistics.median(t1)
+        cpu = {"value": round(wl.batch / t, 2), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{len(times)} full {wl.name} decode steps (B={wl.batch}) on instance 0, "
-                         f"fp64, median {t:.2f}s",
-               "gbps": round(step_bytes / t / 1e9, 3)}
+                         f"fp64, median {t:.2f}s; 3 more on one thread, median {t1:.2f}s",
+               "gbps": round(step_bytes / t / 1e9, 3),
+               "value_1_thread": round(wl.batch / t1, 2),
+               "cpu_model": cpu_model()}
 
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
     cfg = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "n_q_heads": wl.n_q_heads,

@@ -411,3 +411,12 @@ int orc_max_threads(void) {
     return 1;
 #endif
 }
+
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

@@ -57,5 +57,7 @@ void orc_decode_step(const orc_problem *pr, const void *q, const void *landmarks
                      const int32_t *k_per_seq, double *scores, int32_t *indices, int32_t *n_sel,
                      double *out, double *lse, double *overlap);
 int orc_max_threads(void);
+/* Threads the following calls use (OpenMP over independent (b, g) pairs). */
+void orc_set_threads(int n);
 
 #endif

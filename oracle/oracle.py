@@ -52,6 +52,7 @@ def lib():
         L.orc_e4m3fn_value.restype = C.c_double
         L.orc_e4m3fn_value.argtypes = [C.c_uint8]
         L.orc_max_threads.restype = C.c_int
+        L.orc_set_threads.argtypes = [C.c_int]
         L.orc_partial.argtypes = [C.POINTER(Problem)] + [C.c_void_p] * 6 + [
             C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
         L.orc_merge.argtypes = [C.c_int, C.c_int] + [C.c_void_p] * 4
@@ -193,3 +194,7 @@ def decode_step(pr: Problem, q, landmarks, k_pool, v_pool, k_scales, v_scales, b
 
 def max_threads() -> int:
     return lib().orc_max_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(n)
