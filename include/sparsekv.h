@@ -133,6 +133,14 @@ typedef struct {
 const char *sparsekv_status_string(int status);
 /* Text of the last SKV_E_HIP / validation failure on the calling thread. */
 const char *sparsekv_last_error(void);
+/*
+ * Every kernel takes its parameters by value, and each workgroup reads them
+ * before its first memory access.  Run with the HIP runtime's kernel
+ * arguments in device memory (HIP_FORCE_DEV_KERNARG=1 in the environment
+ * before the runtime starts): kept in host memory they cost a host-link round
+ * trip per launch, measured at 3.3 us (5%) on the 32k-context decode step.
+ */
+
 /* Library version as "major.minor.patch". */
 const char *sparsekv_version(void);
 
