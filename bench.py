@@ -447,6 +447,20 @@ def main() -> int:
     wall_ms = (wall1 - wall0) * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f} us)")
 
+    # per-step spread: a separate pass with an event after every step (the
+    # events sit between launches and add about 2 us per step, so this pass
+    # gives the spread, not the rate)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for k in range(args.steps):
+        one_step(k)
+        evs[k + 1].record(stream)
+    evs[-1].synchronize()
+    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(args.steps))
+
+    def pct(q: float) -> float:
+        return round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 2)
+
     lens = steps[0].inp.seq_lens.cpu().numpy()
     kps = steps[0].inp.k_per_seq.cpu().numpy()
     step_bytes = configs.algorithmic_bytes(wl, lens, kps)
@@ -513,7 +527,7 @@ def main() -> int:
             O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
             times.append(time.perf_counter() - t0)
             spent = time.perf_counter() - t_start
-            if len(times) >= 50 or (len(times) >= 3 and spent > args.cpu_budget):
+            if len(times) >= 100 or (len(times) >= 3 and spent > args.cpu_budget):
                 break
         t = statistics.median(times)
         threads = O.max_threads()
@@ -529,7 +543,7 @@ def main() -> int:
         cpu = {"value": round(wl.batch / t, 2), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{len(times)} full {wl.name} decode steps (B={wl.batch}) on instance 0, "
-                         f"fp64, median {t:.2f}s; 3 more on one thread, median {t1:.2f}s",
+                         f"fp64, median {t * 1e3:.1f} ms; 3 more on one thread, median {t1 * 1e3:.1f} ms",
                "gbps": round(step_bytes / t / 1e9, 3),
                "value_1_thread": round(wl.batch / t1, 2),
                "cpu_model": cpu_model()}
@@ -559,6 +573,7 @@ def main() -> int:
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBS, 4),
         "wall_ms_per_step": round(wall_ms, 5),
+        "step_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "launches_per_step": launches,
         "roofline": roofline,
         "cpu_baseline": cpu,
