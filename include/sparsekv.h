@@ -152,7 +152,7 @@ const char *sparsekv_version(void);
  * achieved bandwidth can be compared with.  `buffer` and `bytes` must be
  * multiples of 16 (else SKV_E_SHAPE).  `sink` is a device buffer of
  * `sink_bytes` (at least 4, 4-aligned); it bounds the grid at one workgroup
- * per word (16 KiB read per workgroup when there are enough words) and is
+ * per word (512 threads and 32 KiB per workgroup, at most 32768) and is
  * written only if a workgroup's folded data equals one fixed 32-bit value, so
  * its contents carry no meaning.  Asynchronous on `stream`; allocates nothing.
  */

@@ -165,9 +165,9 @@ hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_lse_merge(const float* o_a, const float* lse_a, const float* o_b, const float* lse_b,
                             float* out, float* lse, int rows, int D, hipStream_t s);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
-// Streaming read of `bytes` (a multiple of 16) with one workgroup per 16 KiB,
-// at most sink_words workgroups; sink[workgroup] is written only in the
-// improbable case noted at the kernel.
+// Streaming read of `bytes` (a multiple of 16) with one 512-thread workgroup
+// per 32 KiB, at most 32768 and at most sink_words workgroups;
+// sink[workgroup] is written only in the improbable case noted at the kernel.
 hipError_t launch_stream_read(const void* ptr, size_t bytes, uint32_t* sink, int sink_words, hipStream_t s);
 
 // LDS bytes of a scoring workgroup: qbar [T][d] floats, keys [T][score_cols]
