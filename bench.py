@@ -461,9 +461,11 @@ def main() -> int:
     def pct(q: float) -> float:
         return round(per_step[min(len(per_step) - 1, int(q * len(per_step)))], 2)
 
-    lens = steps[0].inp.seq_lens.cpu().numpy()
-    kps = steps[0].inp.k_per_seq.cpu().numpy()
-    step_bytes = configs.algorithmic_bytes(wl, lens, kps)
+    # the steps rotate over the instances, whose lengths differ for ragged
+    # batches: a step moves the mean of their algorithmic bytes
+    shapes = [(st.inp.seq_lens.cpu().numpy(), st.inp.k_per_seq.cpu().numpy()) for st in steps]
+    bytes_per_instance = [configs.algorithmic_bytes(wl, L, K) for L, K in shapes]
+    step_bytes = statistics.mean(bytes_per_instance)
     tokens_per_s = wl.batch * n_layers / (ms_per_step * 1e-3)
 
     # ---- dominant kernel: the step itself when it is one launch, else the
@@ -544,7 +546,7 @@ def main() -> int:
                "kind": "oracle",
                "sample": f"{len(times)} full {wl.name} decode steps (B={wl.batch}) on instance 0, "
                          f"fp64, median {t * 1e3:.1f} ms; 3 more on one thread, median {t1 * 1e3:.1f} ms",
-               "gbps": round(step_bytes / t / 1e9, 3),
+               "gbps": round(bytes_per_instance[0] / t / 1e9, 3),
                "value_1_thread": round(wl.batch / t1, 2),
                "cpu_model": cpu_model()}
 
@@ -570,6 +572,7 @@ def main() -> int:
         "data": "synthetic",
         "config": cfg,
         "step_bytes": int(step_bytes),
+        "step_bytes_per_instance": [int(x) for x in bytes_per_instance],
         "step_gbps": round(step_gbps, 1),
         "step_frac_of_peak": round(step_gbps / HBM_PEAK_GBS, 4),
         "wall_ms_per_step": round(wall_ms, 5),
@@ -582,7 +585,7 @@ def main() -> int:
         line["overlap_mean"] = round(float(steps[0].overlap.mean().item()), 4)
     if wl.pool == "host":
         # the gather's pull over the host link, against a contiguous pinned copy
-        link_bytes = n_layers * configs.host_link_bytes(wl, lens, kps)
+        link_bytes = n_layers * statistics.mean(configs.host_link_bytes(wl, L, K) for L, K in shapes)
         link_gbps = link_bytes / (ms_per_step * 1e-3) / 1e9
         ceiling = h2d_ceiling_gbps()
         line["host_link"] = {"bytes_per_step": int(link_bytes), "gbps": round(link_gbps, 2),
