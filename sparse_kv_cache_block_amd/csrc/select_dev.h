@@ -66,7 +66,7 @@ struct TopkShared {
   uint32_t hist1[2][256];   // the second token's, when two tokens select side by side
   uint32_t scan_w[2][NT / kWave];
   uint32_t ov_w[NT / kWave];          // list_overlap's per-wave hit counts
-  uint32_t digit, above, exact, common;
+  uint32_t digit, above, exact;
   uint32_t digit2[2], above2[2], exact2[2];
 };
 
