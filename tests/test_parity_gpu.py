@@ -165,6 +165,18 @@ def test_two_tokens_many_candidates_few_pairs():
     check_step(wl, gen_device="cuda")
 
 
+@pytest.mark.parametrize("k", [200, 16], ids=["one_level", "two_levels"])
+def test_two_tokens_at_the_block_limit(k):
+    """16384 blocks per sequence (the most the library takes), two tokens, 2
+    pairs, 16380 candidates.  k 200 exceeds a chunk's 128 rows, so the last
+    workgroup selects over all 2 x 16380 published scores in LDS (about 135 KB);
+    k 16 takes two levels with the candidates' ids read back from the workspace."""
+    wl = configs.DUAL.scaled(batch=1, n_q_heads=16, n_kv_heads=2, block_size=16, context=262144,
+                             window=64, top_k=k)
+    assert wl.max_blocks == 16384
+    check_step(wl, gen_device="cuda")
+
+
 # 2 sequences x 2 KV heads, 4080 candidates, k 16: each of 64 scoring workgroups
 # per pair keeps its own top 16 (1024 candidates) and the last one selects
 TWO_LEVEL = configs.LLAMA32K.scaled(batch=2, n_q_heads=8, n_kv_heads=2, context=131072, top_k=16)
