@@ -15,7 +15,11 @@
 // order-preserving 32-bit keys (four 8-bit passes) finds the k-th largest key;
 // blocks above it are kept, blocks equal to it are kept in ascending id order
 // until k are chosen (ties to the lowest id), and the chosen ids are written
-// in ascending order after one block-wide scan.
+// in ascending order after one block-wide scan.  When a pair's scoring rows
+// are split over several workgroups, each may first keep its own top k (a
+// block of the pair's top k is always among its chunk's top k under the same
+// order) and the last to finish selects among those candidates
+// (select_scored).
 //
 // NT is the workgroup size.  PUB selects device-scope atomic stores for the
 // selection results, for readers in other workgroups of the same launch.
