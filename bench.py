@@ -219,6 +219,55 @@ def gather_correct_probe(reps: int) -> int:
     return 0
 
 
+def hbm_gather_probe(reps: int, instances: int) -> int:
+    """llama32k workload: the stand-alone gather of the selected K/V chunks from
+    the HBM pool into staging buffers (in the decode step this gather is fused
+    into the attention's loads and never copied).  Rotates over `instances`
+    input sets, each with its own stage."""
+    import torch
+
+    from sparse_kv_cache_block_amd import binding as B
+    from sparse_kv_cache_block_amd import configs
+    from sparse_kv_cache_block_amd.inputs import make_inputs
+    from sparse_kv_cache_block_amd.step import DecodeStep
+
+    wl = configs.LLAMA32K
+    torch.cuda.set_device(0)
+    sets = []
+    for i in range(instances):
+        st = DecodeStep(make_inputs(wl, device="cuda", instance=i))
+        st.run()
+        shape = (wl.batch, wl.n_kv_heads, st.pr.k_max, wl.block_size, wl.head_dim)
+        sets.append((st, torch.empty(shape, dtype=st.inp.k_pool.dtype, device="cuda"),
+                     torch.empty(shape, dtype=st.inp.v_pool.dtype, device="cuda")))
+    torch.cuda.synchronize()
+
+    def gather(k: int) -> None:
+        st, ks, vs = sets[k % len(sets)]
+        d = st.inp
+        B.sparsekv_gather(st.pr, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table, st.indices,
+                          st.n_sel, ks, vs, None, None)
+
+    for k in range(5):
+        gather(k)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for k in range(reps):
+        gather(k)
+    ev[1].record()
+    ev[1].synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+    chunks = int(sets[0][0].n_sel[:, 0].sum())
+    moved = chunks * 2 * wl.block_size * wl.head_dim * 2   # K and V chunks, bf16
+    print(json.dumps({
+        "probe": "hbm_gather", "workload": "llama32k (B32, 8 KV heads, k64, blk32, bf16, HBM pool)",
+        "reps": reps, "instances": instances, "us_per_gather": round(us, 2), "chunks": chunks,
+        "bytes_read": moved, "bytes_written": moved,
+        "read_gbps": round(moved / (us * 1e-6) / 1e9, 1),
+        "read_plus_write_gbps": round(2 * moved / (us * 1e-6) / 1e9, 1)}), flush=True)
+    return 0
+
+
 def cobatched_probe(reps: int, instances: int) -> int:
     """Dual workload: both query tokens attended by one co-batched launch over
     the union of their selections, against one attention launch per token."""
@@ -370,6 +419,8 @@ def main() -> int:
                     help="only compare the full host gather with the speculative correction and exit")
     ap.add_argument("--hybrid", action="store_true",
                     help="only compare the hybrid CPU-GPU step with the all-GPU host-pool step and exit")
+    ap.add_argument("--gather", action="store_true",
+                    help="only time the stand-alone gather from the HBM pool (llama32k) and exit")
     ap.add_argument("--cobatched", action="store_true",
                     help="only compare co-batched two-token attention with one launch per token and exit")
     args = ap.parse_args()
@@ -379,6 +430,8 @@ def main() -> int:
         return gather_correct_probe(max(1, min(args.steps, 50)))
     if args.cobatched:
         return cobatched_probe(max(1, args.steps), max(1, args.instances))
+    if args.gather:
+        return hbm_gather_probe(max(1, args.steps), max(1, args.instances))
     if args.hybrid:
         return hybrid_probe(max(1, min(args.steps, 50)))
 
