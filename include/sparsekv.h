@@ -149,8 +149,9 @@ const char *sparsekv_version(void);
  * at `buffer` once with the same 16-byte non-temporal loads the step's
  * kernels use, four per thread in flight, so that the rate it reaches on a
  * buffer far larger than the caches is the streaming-read ceiling the step's
- * achieved bandwidth can be compared with.  `buffer` and `bytes` must be
- * multiples of 16 (else SKV_E_SHAPE).  `sink` is a device buffer of
+ * achieved bandwidth can be compared with.  `buffer` must be 16-byte aligned
+ * and `bytes` a multiple of 16 (else SKV_E_SHAPE); a NULL `buffer` or `sink`
+ * gives SKV_E_NULL, a launch failure SKV_E_HIP.  `sink` is a device buffer of
  * `sink_bytes` (at least 4, 4-aligned); it bounds the grid at one workgroup
  * per word (512 threads and 32 KiB per workgroup, at most 32768) and is
  * written only if a workgroup's folded data equals one fixed 32-bit value, so
@@ -160,8 +161,9 @@ skv_status sparsekv_stream_read(const void *buffer, size_t bytes, void *sink, si
                                 void *stream);
 
 /*
- * Workspace: device scratch for split partials, score staging and arrival
- * counters.  sparsekv_workspace_size() gives the bytes needed by
+ * Workspace: device scratch for split partials, score staging (or, for a
+ * selection over split scoring rows, each chunk's own top-k candidates) and
+ * arrival counters.  sparsekv_workspace_size() gives the bytes needed by
  * sparsekv_attend / sparsekv_decode_step / sparsekv_decode_layers for a
  * problem.  A new workspace must be cleared once with sparsekv_workspace_init
  * (a fill kernel, safe inside graph capture); every call returns its counters
