@@ -173,7 +173,7 @@ def gather_correct_probe(reps: int) -> int:
     from sparse_kv_cache_block_amd import binding as B
     from sparse_kv_cache_block_amd import configs
     from sparse_kv_cache_block_amd.inputs import make_inputs
-    from sparse_kv_cache_block_amd.step import DecodeStep, to_device_for
+    from sparse_kv_cache_block_amd.step import DecodeStep, LayerPipeline, to_device_for
 
     wl = configs.HOST.scaled(n_q_tokens=2, spec_noise=0.3)
     torch.cuda.set_device(0)
@@ -449,7 +449,7 @@ def main() -> int:
     from sparse_kv_cache_block_amd import binding as B
     from sparse_kv_cache_block_amd import configs
     from sparse_kv_cache_block_amd.inputs import make_inputs
-    from sparse_kv_cache_block_amd.step import DecodeStep, to_device_for
+    from sparse_kv_cache_block_amd.step import DecodeStep, LayerPipeline, to_device_for
 
     wl = configs.get(args.workload)
     torch.cuda.set_device(0)
@@ -472,13 +472,15 @@ def main() -> int:
 
     n_layers = wl.n_layers if wl.pool == "host" else 1
     copy_stream = torch.cuda.Stream() if wl.pool == "host" else None
+    # host pool: n_layers layer-steps sharing the instance's pool, landmarks and
+    # query, through the two-slot staging pipeline
+    pipes = [LayerPipeline([st.inp] * n_layers) for st in steps] if wl.pool == "host" else None
 
     def one_step(k: int) -> None:
-        st = steps[k % len(steps)]
-        if wl.pool == "host":
-            st.run_layers(n_layers, copy_stream=copy_stream)
+        if pipes:
+            pipes[k % len(pipes)].run(copy_stream=copy_stream)
         else:
-            st.run()
+            steps[k % len(steps)].run()
 
     for k in range(args.warmup):
         one_step(k)

@@ -57,7 +57,19 @@
  *
  * Supported: d in {64, 128}; blk in {16, 32, 64}; 1 <= G <= 8; T in {1, 2};
  * kv fp32 with q fp32, or kv bf16 / fp8 e4m3fn with q bf16; landmarks fp32 or
- * bf16; max_blocks <= 16384; k_max <= max_blocks.
+ * bf16; max_blocks <= 16384; k_max <= max_blocks.  The selection keeps a
+ * pair's keys in one workgroup's 160 KiB of LDS, which bounds k_max further
+ * (SKV_E_UNSUPPORTED before any launch beyond it):
+ *   steps that select (decode_step when it takes two or three launches,
+ *   decode_layers*, the hybrid step):
+ *     4 * (T*d + T*C + 2*k_max + 512) + 4232 <= 163840 bytes,
+ *     C = max_blocks - floor(W / blk) (the most candidates a sequence has);
+ *     e.g. T = 2, d = 128, C = 16380: k_max <= 3187;  T = 1: k_max <= 11441;
+ *   sparsekv_topk: 4 * (max_blocks + 2*k_max) + 4232 <= 163840 bytes,
+ *     e.g. max_blocks = 16384: k_max <= 11759.
+ * Alignment: q, landmarks, K/V pools, stages and window buffers are read with
+ * 16-byte loads, so their addresses, pool_stride_block * element size and
+ * pool_stride_head * element size must be multiples of 16 (SKV_E_SHAPE).
  */
 #ifndef SPARSEKV_H
 #define SPARSEKV_H
@@ -374,6 +386,55 @@ skv_status sparsekv_decode_layers(const skv_problem *pr, int32_t n_layers,
                                   float *const *k_stage_scales, float *const *v_stage_scales,
                                   void *workspace, size_t workspace_bytes,
                                   void *stream, void *copy_stream);
+
+/*
+ * A layer's predicted selection for sparsekv_decode_layers_predicted: an
+ * earlier selection in the layout sparsekv_topk writes ([B][T][Hkv][k_max]
+ * ids ascending within n_sel, n_sel [B][T][Hkv]), of which row `token` is
+ * the prediction -- for a two-token problem, the speculative token's row
+ * (token 1) of the previous decode step's outputs for this layer.
+ */
+typedef struct {
+    const int32_t *indices;
+    const int32_t *n_sel;
+    int32_t token;
+    int32_t *misses;             /* [B][Hkv]: real blocks the prediction missed; may be NULL */
+} skv_layer_prediction;
+
+/*
+ * Host-pool layer pipeline with prefetch by a predicted index (DualDecoder
+ * review: mechanism summary -- blocks are prefetched by the index a
+ * speculative token predicts, with a lead of two layers, and the blocks it
+ * missed are fetched on demand; Fig. 19 -- predicted blocks fetched
+ * contiguously, then reordered on the GPU into the real index's order;
+ * Fig. 11 -- a two-slot ping-pong staging buffer).
+ *   copy_stream: the predicted blocks of layer l (pred[l], a plain gather)
+ *     go into prefetch slot l % 2 (pref_k / pref_v [2], and pref_k_scales /
+ *     pref_v_scales [2] for fp8), as soon as layer l-2's correction has read
+ *     that slot, so prefetches run up to two layers ahead of the compute;
+ *   stream, per layer in order: scoring and top-k of layer l (its real
+ *     selection, into out[l]); then, once layer l's prefetch is staged, the
+ *     correction (sparsekv_gather_correct's kernel): blocks the prediction
+ *     holds move from the prefetch slot into k_stage / v_stage in the real
+ *     selection's order, the misses are read from the pinned pool; then the
+ *     attention of the stage plus the HBM window buffers.
+ * The misses are fetched on `stream`, directly before the attention that
+ * needs them, so no background prefetch is queued ahead of them.  Each
+ * layer's results equal sparsekv_decode_step's on in[l] (the stage holds the
+ * real selection's gather byte for byte, whatever the prediction).  The
+ * stage must not overlap a prefetch slot (SKV_E_SHAPE).  The copy stream
+ * starts after the work already queued on `stream`; `stream` ends after
+ * every layer's attention, which follows every prefetch.
+ */
+skv_status sparsekv_decode_layers_predicted(const skv_problem *pr, int32_t n_layers,
+                                            const skv_step_inputs *in, const skv_step_outputs *out,
+                                            const skv_layer_prediction *pred,
+                                            void *const *pref_k, void *const *pref_v,
+                                            float *const *pref_k_scales, float *const *pref_v_scales,
+                                            void *k_stage, void *v_stage,
+                                            float *k_stage_scales, float *v_stage_scales,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream, void *copy_stream);
 
 #ifdef __cplusplus
 }

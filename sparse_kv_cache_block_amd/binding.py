@@ -27,7 +27,7 @@ EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
             "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
             "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid", "sparsekv_host_attention",
-            "sparsekv_stream_read")
+            "sparsekv_stream_read", "sparsekv_decode_layers_predicted")
 
 
 class SkvError(RuntimeError):
@@ -70,6 +70,11 @@ class HostPart(C.Structure):
                 ("v_scales", C.c_void_p), ("o", C.c_void_p), ("lse", C.c_void_p)]
 
 
+class LayerPrediction(C.Structure):
+    _fields_ = [("indices", C.c_void_p), ("n_sel", C.c_void_p), ("token", C.c_int32),
+                ("misses", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -108,6 +113,10 @@ def lib() -> C.CDLL:
             "sparsekv_decode_layers": (C.c_int, [P, C.c_int32, C.POINTER(StepInputs),
                                                  C.POINTER(StepOutputs), C.POINTER(vp), C.POINTER(vp),
                                                  C.POINTER(vp), C.POINTER(vp), vp, sz, vp, vp]),
+            "sparsekv_decode_layers_predicted": (C.c_int, [P, C.c_int32, C.POINTER(StepInputs),
+                                                           C.POINTER(StepOutputs), C.POINTER(LayerPrediction),
+                                                           C.POINTER(vp), C.POINTER(vp), C.POINTER(vp),
+                                                           C.POINTER(vp), vp, vp, vp, vp, vp, sz, vp, vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -278,6 +287,29 @@ def sparsekv_decode_layers(pr: Problem, inputs: Sequence[StepInputs], outputs: S
                                         kss, vss, _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
                                         _stream(stream), cs), "sparsekv_decode_layers")
+
+
+def layer_prediction(indices, n_sel, token: int, misses=None) -> LayerPrediction:
+    return LayerPrediction(_ptr(indices), _ptr(n_sel), int(token), _ptr(misses))
+
+
+def sparsekv_decode_layers_predicted(pr: Problem, inputs: Sequence[StepInputs], outputs: Sequence[StepOutputs],
+                                     predictions: Sequence[LayerPrediction], pref_k: Sequence, pref_v: Sequence,
+                                     k_stage, v_stage, workspace: torch.Tensor,
+                                     pref_k_scales: Optional[Sequence] = None,
+                                     pref_v_scales: Optional[Sequence] = None, k_stage_scales=None,
+                                     v_stage_scales=None, stream=None, copy_stream=None) -> None:
+    n = len(inputs)
+    InArr, OutArr, PredArr, PtrArr = StepInputs * n, StepOutputs * n, LayerPrediction * n, C.c_void_p * 2
+    pk = PtrArr(*(_ptr(x) for x in pref_k))
+    pv = PtrArr(*(_ptr(x) for x in pref_v))
+    pks = PtrArr(*(_ptr(x) for x in pref_k_scales)) if pref_k_scales else None
+    pvs = PtrArr(*(_ptr(x) for x in pref_v_scales)) if pref_v_scales else None
+    cs = None if copy_stream is None else _stream(copy_stream)
+    _check(lib().sparsekv_decode_layers_predicted(
+        C.byref(pr), n, InArr(*inputs), OutArr(*outputs), PredArr(*predictions), pk, pv, pks, pvs,
+        _ptr(k_stage), _ptr(v_stage), _ptr(k_stage_scales), _ptr(v_stage_scales), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream), cs), "sparsekv_decode_layers_predicted")
 
 
 # ---------------------------------------------------------------- helpers

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
       p, smem, b, g, first, count, count, 0,
       [&](int item) { return describe<KV, D, BLK>(p, b, g, item, nsel, ws); },
       [](int) { return ItemDesc{0, 0, 0}; }, [] {}, [](auto&& issue_first) { issue_first(); }, [] {});
-  attend_finish<KV, D, BLK, kAttnWaves>(p, smem, b, g, split, p.n_splits, &s_last, nullptr);
+  attend_finish<KV, D, BLK, kAttnWaves>(p, smem, b, g, split, p.n_splits, &s_last);
 }
 
 // First index of the ascending a[0..n) holding a value >= x.
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_cobatched_kernel(AttnPara
         return describe_window<KV, D, BLK>(p, b, g, bi - nu, sub, ws);
       },
       [](int) { return ItemDesc{0, 0, 0}; }, [] {}, [](auto&& issue_first) { issue_first(); }, [] {});
-  attend_finish<KV, D, BLK, kAttnWaves, 2>(p, smem, b, g, split, p.n_splits, &s_last, nullptr);
+  attend_finish<KV, D, BLK, kAttnWaves, 2>(p, smem, b, g, split, p.n_splits, &s_last);
 }
 
 template <int KV, int D>

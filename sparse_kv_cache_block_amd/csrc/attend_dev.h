@@ -509,13 +509,12 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
 
 // Combine the NW waves' regions into the workgroup's partial for split
 // `split` of n_splits; a single split writes the output directly, otherwise
-// the last split of (b, g) to arrive merges all of them.  `ready`, when given,
-// is the pair's ready flag, cleared once every split of the pair is done.
+// the last split of (b, g) to arrive merges all of them.
 // With NTOK query tokens the rows are (token, head) pairs and the output row
 // of token t, head h is (b, t, gG + h) of out [B][NTOK][Hq][d].
 template <int KV, int D, int BLK, int NW, int NTOK = 1>
 __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, int b, int g, int split,
-                                              int n_splits, int* s_last, unsigned* ready) {
+                                              int n_splits, int* s_last) {
   using C = AttnCfg<KV, D, BLK>;
   constexpr int NTH = NW * kWave;
   constexpr bool LO_PACKED = NTOK == 1 && KV != KV_F32;
@@ -557,15 +556,10 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
       publish_f32(part + h * (D + 2) + 1, Ls);
     }
   }
-  if (n_splits == 1) {
-    if (ready && threadIdx.x == 0) __hip_atomic_store(ready + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
+  if (n_splits == 1) return;
 
   // ---- the last split of (b, g) merges every split
   if (!arrive_last(p.counters + pair, (unsigned)n_splits, s_last)) return;
-  // every split has passed its wait on the pair's ready flag: clear it for the next launch
-  if (ready && threadIdx.x == 0) __hip_atomic_store(ready + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // each thread merges its outputs over the splits online, reading 8 splits'
   // (max, sum, output) per round of loads: one round for up to 8 splits, and
   // no LDS whatever the split count

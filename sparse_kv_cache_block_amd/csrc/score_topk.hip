@@ -45,6 +45,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(TopkParams p) {
 
 size_t topk_lds_bytes(int max_cand) { return (size_t)max_cand * 4; }
 
+size_t select_static_lds_bytes() { return sizeof(TopkShared<kSelThreads>) + sizeof(int); }
+
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s) {
   const dim3 grid(chunks, p.Hkv, p.B);
   const size_t lds = score_lds_bytes(p.T, p.D, p.score_cols, p.k_max, p.fused_select != 0, false,

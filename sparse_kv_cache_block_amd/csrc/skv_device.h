@@ -155,6 +155,15 @@ __device__ __forceinline__ void lds_barrier() {
 // reads the others' values with device-scope loads.  This avoids an
 // agent-scope fence per workgroup, which on this chip writes back and
 // invalidates the whole L2 of the XCD.
+//
+// The rule this relies on: every value a last arriver reads from another
+// workgroup must have been written with an agent-scope atomic store
+// (publish_f32, put_i32<true> / put_f32<true>), and read with fetch_f32 /
+// fetch_i32.  The counter increment is relaxed, so it orders nothing by
+// itself: a plain store into the split partials or the candidate rows may
+// still sit in the producer's XCD-private L2 when the last arriver (on
+// another XCD) reads, and would be seen stale.  The s_waitcnt below only makes
+// the atomic stores complete at device scope before the increment.
 __device__ __forceinline__ void publish_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

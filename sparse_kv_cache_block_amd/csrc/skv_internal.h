@@ -10,6 +10,24 @@
 
 namespace skv {
 
+// ------------------------------------------------------------------ errors
+// Set the calling thread's error text (sparsekv_last_error) and return st.
+skv_status fail(skv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// SKV_E_HIP with the runtime's text for e.
+skv_status hip_fail(hipError_t e, const char* what);
+
+#define SKV_TRY_HIP(expr, what)                          \
+  do {                                                   \
+    hipError_t e_ = (expr);                              \
+    if (e_ != hipSuccess) return ::skv::hip_fail(e_, what); \
+  } while (0)
+
+#define SKV_TRY(expr)                  \
+  do {                                 \
+    skv_status s_ = (expr);            \
+    if (s_ != SKV_OK) return s_;       \
+  } while (0)
+
 // ------------------------------------------------------------ scoring / top-k
 struct ScoreParams {
   const void* q;            // [B][T][Hq][d]
@@ -130,12 +148,26 @@ struct Plan {
   // there are enough pairs to fill the chip)
   int fused_step;
   size_t step_lds;          // dynamic LDS bytes of the step kernel (scoring region)
+  // scoring with the fused selection (two-launch, host-pool, hybrid and layer
+  // steps): static plus dynamic LDS of its workgroups, and whether that fits
+  size_t select_lds;
+  int select_fits;
   size_t off_score_counters, off_attn_counters, off_scores, off_partials, off_phys;
   size_t off_hybrid;        // hybrid step: the window part's o [B][Hq][d] and lse [B][Hq]
   size_t total_bytes;
 };
 
 Plan make_plan(const skv_problem& pr);
+
+// Host-side checks of a device-pool decode step (problem, step pointers, the
+// selection's LDS); fills *pl.  Issues no HIP call.
+skv_status check_device_step(const skv_problem* pr, const skv_step_inputs* in, const skv_step_outputs* out,
+                             Plan* pl);
+// Enqueue a checked device-pool decode step on workspace ws (pl.total_bytes).
+// With clear_bytes > 0, a fill kernel first zeroes ws[0, clear_bytes); every
+// remaining argument check runs before it.
+skv_status enqueue_device_step(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                               const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes);
 
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);
@@ -194,5 +226,8 @@ constexpr size_t kScoreStaticLds = 8 * 1024;
 
 // LDS bytes the score kernel needs for a fused selection over max_cand keys.
 size_t topk_lds_bytes(int max_cand);
+// Static LDS of the 512-thread scoring / selection kernels (selection state
+// and a flag), next to their dynamic region.
+size_t select_static_lds_bytes();
 
 }  // namespace skv

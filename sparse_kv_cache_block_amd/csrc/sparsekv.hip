@@ -7,17 +7,20 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
+#include <initializer_list>
+#include <mutex>
 
 #include "host_attn.h"
 #include "skv_device.h"
 #include "skv_internal.h"
 
 namespace skv {
+
 namespace {
-
 thread_local char g_err[512] = "";
+}  // namespace
 
-skv_status fail(skv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 skv_status fail(skv_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -30,17 +33,7 @@ skv_status hip_fail(hipError_t e, const char* what) {
   return fail(SKV_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-#define SKV_TRY_HIP(expr, what)                 \
-  do {                                          \
-    hipError_t e_ = (expr);                     \
-    if (e_ != hipSuccess) return hip_fail(e_, what); \
-  } while (0)
-
-#define SKV_TRY(expr)                  \
-  do {                                 \
-    skv_status s_ = (expr);            \
-    if (s_ != SKV_OK) return s_;       \
-  } while (0)
+namespace {
 
 int elem_bytes(int dt) { return dt == SKV_F32 ? 4 : dt == SKV_BF16 ? 2 : 1; }
 
@@ -65,6 +58,11 @@ skv_status check_problem(const skv_problem* pr) {
     if (dt < SKV_F32 || dt > SKV_FP8_E4M3FN) return fail(SKV_E_DTYPE, "unknown dtype code %d", dt);
   if (p.pool_location != SKV_POOL_DEVICE && p.pool_location != SKV_POOL_HOST)
     return fail(SKV_E_SHAPE, "unknown pool_location %d", p.pool_location);
+  // every (block, head) chunk is read with 16-byte loads
+  const int64_t eb = elem_bytes(p.kv_dtype);
+  if ((p.pool_stride_block * eb) % 16 != 0 || (p.pool_stride_head * eb) % 16 != 0)
+    return fail(SKV_E_SHAPE, "pool strides (%lld, %lld elements) are not multiples of 16 bytes",
+                (long long)p.pool_stride_block, (long long)p.pool_stride_head);
   const int G = p.n_q_heads / p.n_kv_heads;
   if (G > 8) return fail(SKV_E_UNSUPPORTED, "group size %d > 8", G);
   if (p.head_dim != 64 && p.head_dim != 128)
@@ -83,6 +81,16 @@ skv_status check_problem(const skv_problem* pr) {
 }
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Buffers read or written with 16-byte vector accesses (queries, landmarks,
+// pools, stages, window buffers) must be 16-byte aligned; NULL passes (the
+// NULL checks are separate).
+skv_status check_align16(const char* where, std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if (reinterpret_cast<uintptr_t>(x) % 16 != 0)
+      return fail(SKV_E_SHAPE, "%s: buffer %p is not 16-byte aligned", where, x);
+  return SKV_OK;
+}
 
 #ifndef SKV_ATTN_TARGET_WGS
 #define SKV_ATTN_TARGET_WGS 256
@@ -158,6 +166,9 @@ Plan make_plan(const skv_problem& p) {
                     step_static_lds_bytes(p) + pl.step_lds <= kLdsPerCu;
   }
 #endif
+  pl.select_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true) +
+                  select_static_lds_bytes();
+  pl.select_fits = pl.select_lds <= kLdsPerWorkgroup;
   size_t off = 0;
   pl.off_score_counters = off;
   off = align256(off + (size_t)pairs * 4);
@@ -231,7 +242,9 @@ AttnParams attn_params(const skv_problem& p, const Plan& pl, const void* q, cons
 skv_status set_source(const skv_problem& p, AttnParams& a, const skv_kv_source* src, bool sparse) {
   if (!src) return fail(SKV_E_NULL, "%s source is NULL", sparse ? "sparse" : "window");
   if (!src->k || !src->v) return fail(SKV_E_NULL, "%s source K/V is NULL", sparse ? "sparse" : "window");
+  SKV_TRY(check_align16(sparse ? "sparse source" : "window source", {src->k, src->v}));
   const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
+  if (!sparse && src->kind == SKV_SRC_WINDOW && fp8) return fail(SKV_E_UNSUPPORTED, "fp8 window buffers");
   if (fp8 && (!src->k_scales || !src->v_scales))
     return fail(SKV_E_NULL, "fp8 %s source needs scales", sparse ? "sparse" : "window");
   if (sparse) {
@@ -251,7 +264,6 @@ skv_status set_source(const skv_problem& p, AttnParams& a, const skv_kv_source* 
     if (src->kind == SKV_SRC_PAGED && !src->block_table)
       return fail(SKV_E_NULL, "paged window source needs a block table");
     if (src->kind == SKV_SRC_WINDOW) {
-      if (fp8) return fail(SKV_E_UNSUPPORTED, "fp8 window buffers");
       if (p.window % p.block_size != 0)
         return fail(SKV_E_SHAPE, "window buffer needs window %% block_size == 0");
     }
@@ -313,28 +325,62 @@ skv_status check_step_io(const skv_problem& p, const skv_step_inputs* in, const 
     return fail(SKV_E_NULL, "host pools need HBM window buffers");
   if (p.kv_dtype == SKV_FP8_E4M3FN && (!in->k_scales || !in->v_scales))
     return fail(SKV_E_NULL, "fp8 pools need scales");
+  SKV_TRY(check_align16("decode step", {in->q, in->landmarks, in->k_pool, in->v_pool, in->window_k,
+                                        in->window_v}));
   return SKV_OK;
 }
 
-skv_status enqueue_attend_paged(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
-                                const skv_step_outputs& out, char* ws, hipStream_t s) {
-  AttnParams a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
+// The scoring launch with the fused selection holds the keys of every
+// candidate of a pair (both tokens), the selected ids and the selection's
+// histograms in one workgroup's LDS.
+skv_status check_select_lds(const skv_problem& p, const Plan& pl) {
+  if (!pl.select_fits)
+    return fail(SKV_E_UNSUPPORTED,
+                "selection needs %zu bytes of LDS (> %zu): %d token(s) x %d candidates with k_max %d",
+                pl.select_lds, kLdsPerWorkgroup, p.n_q_tokens, pl.max_cand, p.k_max);
+  return SKV_OK;
+}
+
+// Attention of a device-pool step's second launch, straight from the pool
+// through the selection's physical blocks; checked, not enqueued.
+skv_status prepare_attend_paged(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                                const skv_step_outputs& out, char* ws, AttnParams* a) {
+  *a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
   skv_kv_source sparse{SKV_SRC_PAGED, in.k_pool, in.v_pool, in.k_scales, in.v_scales, in.block_table};
   skv_kv_source win = in.window_k
       ? skv_kv_source{SKV_SRC_WINDOW, in.window_k, in.window_v, nullptr, nullptr, nullptr}
       : sparse;
-  SKV_TRY(set_source(p, a, &sparse, true));
-  SKV_TRY(set_source(p, a, &win, false));
-  a.indices = out.indices;
-  a.n_sel = out.n_sel;
-  a.phys = reinterpret_cast<const int32_t*>(ws + pl.off_phys);
-  SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  SKV_TRY(set_source(p, *a, &sparse, true));
+  SKV_TRY(set_source(p, *a, &win, false));
+  a->indices = out.indices;
+  a->n_sel = out.n_sel;
+  a->phys = reinterpret_cast<const int32_t*>(ws + pl.off_phys);
+  return SKV_OK;
+}
+
+// Compute units of the current device, queried once per device.
+skv_status compute_units(int* cus) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  SKV_TRY_HIP(hipGetDevice(&dev), "device query");
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return SKV_OK;
+    }
+  }
+  int c = 0;
+  SKV_TRY_HIP(hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev), "device query");
+  if (dev >= 0 && dev < kMaxDevices) cache[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
   return SKV_OK;
 }
 
 // The whole device-pool step as one launch (step.hip).
 skv_status enqueue_step(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
-                        const skv_step_outputs& out, char* ws, hipStream_t s) {
+                        const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes) {
   ScoreParams sp = score_params(p, in.q, in.landmarks, in.seq_lens);
   sp.scores = reinterpret_cast<float*>(ws + pl.off_scores);
   sp.score_cols = pl.max_cand > 0 ? pl.max_cand : 1;
@@ -356,10 +402,10 @@ skv_status enqueue_step(const skv_problem& p, const Plan& pl, const skv_step_inp
   a.indices = out.indices;
   a.n_sel = out.n_sel;
   a.n_splits = 1;
-  int dev = 0, cus = 0;
-  SKV_TRY_HIP(hipGetDevice(&dev), "device query");
-  SKV_TRY_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "device query");
+  int cus = 0;
+  SKV_TRY(compute_units(&cus));
   a.longest_first = p.batch * p.n_kv_heads > cus;
+  if (clear_bytes) SKV_TRY_HIP(launch_fill_zero(ws, clear_bytes, s), "workspace clear");
   SKV_TRY_HIP(launch_step(sp, a, pl.step_lds, s), "decode step launch");
   return SKV_OK;
 }
@@ -394,32 +440,47 @@ GatherParams gather_params(const skv_problem& p, const void* k_pool, const void*
   return gp;
 }
 
-skv_status enqueue_host_layer(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+// A host-pool layer's gather (pinned pool -> stage slot) and attention (stage
+// plus HBM window buffers), with every argument checked; nothing is enqueued.
+struct HostLayer {
+  GatherParams gp;
+  AttnParams a;
+};
+
+skv_status prepare_host_layer(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
                               const skv_step_outputs& out, void* k_stage, void* v_stage,
-                              float* k_stage_scales, float* v_stage_scales, char* ws,
-                              hipStream_t s, hipStream_t cs, hipEvent_t ev_sel, hipEvent_t ev_gather,
-                              hipEvent_t slot_free) {
-  // the copy stream waits for this layer's indices (and for the slot to be free)
-  SKV_TRY_HIP(hipEventRecord(ev_sel, s), "event record");
-  SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel, 0), "stream wait");
-  if (slot_free) SKV_TRY_HIP(hipStreamWaitEvent(cs, slot_free, 0), "stream wait");
-  GatherParams gp = gather_params(p, in.k_pool, in.v_pool, in.k_scales, in.v_scales, in.block_table,
-                                  out.indices, out.n_sel, k_stage, v_stage, k_stage_scales, v_stage_scales);
-  SKV_TRY_HIP(launch_gather(gp, cs), "gather launch");
-  SKV_TRY_HIP(hipEventRecord(ev_gather, cs), "event record");
-  SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather, 0), "stream wait");
-  AttnParams a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
+                              float* k_stage_scales, float* v_stage_scales, char* ws, HostLayer* hl) {
+  if (!k_stage || !v_stage) return fail(SKV_E_NULL, "host pools need staging buffers");
+  if (p.kv_dtype == SKV_FP8_E4M3FN && (!k_stage_scales || !v_stage_scales))
+    return fail(SKV_E_NULL, "fp8 staging needs scale buffers");
+  SKV_TRY(check_align16("staging", {k_stage, v_stage}));
+  hl->gp = gather_params(p, in.k_pool, in.v_pool, in.k_scales, in.v_scales, in.block_table, out.indices,
+                         out.n_sel, k_stage, v_stage, k_stage_scales, v_stage_scales);
+  hl->a = attn_params(p, pl, in.q, in.seq_lens, out.out, out.lse, ws);
   skv_kv_source sparse{SKV_SRC_STAGED, k_stage, v_stage, k_stage_scales, v_stage_scales, nullptr};
-  SKV_TRY(set_source(p, a, &sparse, true));
+  SKV_TRY(set_source(p, hl->a, &sparse, true));
   if (p.window > 0) {
     skv_kv_source win{SKV_SRC_WINDOW, in.window_k, in.window_v, nullptr, nullptr, nullptr};
-    SKV_TRY(set_source(p, a, &win, false));
+    SKV_TRY(set_source(p, hl->a, &win, false));
   } else {
-    a.window_kind = SKV_SRC_WINDOW;  // no window splits are launched
+    hl->a.window_kind = SKV_SRC_WINDOW;  // no window splits are launched
   }
-  a.indices = out.indices;
-  a.n_sel = out.n_sel;
-  SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  hl->a.indices = out.indices;
+  hl->a.n_sel = out.n_sel;
+  return SKV_OK;
+}
+
+// Gather on the copy stream once the layer's indices exist (ev_sel, recorded
+// by the caller after the selection) and, if given, once slot_free has
+// fired; attention on the compute stream once the gather is done.
+skv_status enqueue_host_layer(const HostLayer& hl, hipStream_t s, hipStream_t cs, hipEvent_t ev_sel,
+                              hipEvent_t ev_gather, hipEvent_t slot_free) {
+  SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel, 0), "stream wait");
+  if (slot_free) SKV_TRY_HIP(hipStreamWaitEvent(cs, slot_free, 0), "stream wait");
+  SKV_TRY_HIP(launch_gather(hl.gp, cs), "gather launch");
+  SKV_TRY_HIP(hipEventRecord(ev_gather, cs), "event record");
+  SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather, 0), "stream wait");
+  SKV_TRY_HIP(launch_attend(hl.a, s), "attention launch");
   return SKV_OK;
 }
 
@@ -439,6 +500,29 @@ struct EventSet {
 };
 
 }  // namespace
+
+skv_status check_device_step(const skv_problem* pr, const skv_step_inputs* in, const skv_step_outputs* out,
+                             Plan* pl) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  if (p.pool_location != SKV_POOL_DEVICE) return fail(SKV_E_UNSUPPORTED, "device pools only");
+  SKV_TRY(check_step_io(p, in, out));
+  *pl = make_plan(p);
+  if (!pl->fused_step) SKV_TRY(check_select_lds(p, *pl));
+  return SKV_OK;
+}
+
+skv_status enqueue_device_step(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
+                               const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes) {
+  if (pl.fused_step) return enqueue_step(p, pl, in, out, ws, s, clear_bytes);
+  AttnParams a;
+  SKV_TRY(prepare_attend_paged(p, pl, in, out, ws, &a));
+  if (clear_bytes) SKV_TRY_HIP(launch_fill_zero(ws, clear_bytes, s), "workspace clear");
+  SKV_TRY(enqueue_score_select(p, pl, in, out, ws, s));
+  SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  return SKV_OK;
+}
+
 }  // namespace skv
 
 using namespace skv;
@@ -500,6 +584,7 @@ skv_status sparsekv_score(const skv_problem* pr, const void* q, const void* land
                           const int32_t* seq_lens, float* scores, void* stream) {
   SKV_TRY(check_problem(pr));
   if (!q || !landmarks || !seq_lens || !scores) return fail(SKV_E_NULL, "score: NULL argument");
+  SKV_TRY(check_align16("score", {q, landmarks}));
   const skv_problem& p = *pr;
   ScoreParams sp = score_params(p, q, landmarks, seq_lens);
   sp.scores = scores;
@@ -520,9 +605,14 @@ skv_status sparsekv_topk(const skv_problem* pr, const float* scores, const int32
                          const int32_t* k_per_seq, int32_t* indices, int32_t* n_sel, float* overlap,
                          void* stream) {
   SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  // one workgroup holds a row's keys and the selected ids in LDS
+  const size_t lds = topk_lds_bytes(p.max_blocks_per_seq) + (size_t)2 * p.k_max * 4 + select_static_lds_bytes();
+  if (lds > kLdsPerWorkgroup)
+    return fail(SKV_E_UNSUPPORTED, "topk needs %zu bytes of LDS (> %zu): max_blocks %d, k_max %d", lds,
+                kLdsPerWorkgroup, p.max_blocks_per_seq, p.k_max);
   if (!scores || !seq_lens || !k_per_seq || !indices || !n_sel)
     return fail(SKV_E_NULL, "topk: NULL argument");
-  const skv_problem& p = *pr;
   TopkParams tp{};
   tp.scores = scores;
   tp.seq_lens = seq_lens;
@@ -552,6 +642,7 @@ skv_status sparsekv_gather(const skv_problem* pr, const void* k_pool, const void
   const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
   if (fp8 && (!k_scales || !v_scales || !k_stage_scales || !v_stage_scales))
     return fail(SKV_E_NULL, "gather: fp8 needs pool and stage scales");
+  SKV_TRY(check_align16("gather", {k_pool, v_pool, k_stage, v_stage}));
   GatherParams gp = gather_params(p, k_pool, v_pool, k_scales, v_scales, block_table, indices, n_sel,
                                   k_stage, v_stage, k_stage_scales, v_stage_scales);
   SKV_TRY_HIP(launch_gather(gp, as_stream(stream)), "gather launch");
@@ -580,6 +671,7 @@ skv_status sparsekv_gather_correct(const skv_problem* pr, const void* k_pool, co
   if (fp8 && (!k_scales || !v_scales || !k_stage_scales || !v_stage_scales || !spec_k_scales ||
               !spec_v_scales))
     return fail(SKV_E_NULL, "gather_correct: fp8 needs pool and stage scales");
+  SKV_TRY(check_align16("gather_correct", {k_pool, v_pool, spec_k_stage, spec_v_stage, k_stage, v_stage}));
   const size_t stage_bytes = (size_t)p.batch * p.n_kv_heads * p.k_max * p.block_size * p.head_dim *
                              elem_bytes(p.kv_dtype);
   auto overlaps = [&](const void* a, const void* b) {
@@ -611,6 +703,7 @@ skv_status sparsekv_attend(const skv_problem* pr, const void* q, const skv_kv_so
   SKV_TRY(check_problem(pr));
   const skv_problem& p = *pr;
   if (!q || !indices || !n_sel || !seq_lens || !out) return fail(SKV_E_NULL, "attend: NULL argument");
+  SKV_TRY(check_align16("attend", {q}));
   const Plan pl = make_plan(p);
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
   char* ws = static_cast<char*>(workspace);
@@ -635,6 +728,7 @@ skv_status sparsekv_attend_cobatched(const skv_problem* pr, const void* q, const
     return sparsekv_attend(pr, q, sparse, indices, n_sel, window, seq_lens, out, lse, workspace,
                            workspace_bytes, stream);
   if (!q || !indices || !n_sel || !seq_lens || !out) return fail(SKV_E_NULL, "attend_cobatched: NULL argument");
+  SKV_TRY(check_align16("attend_cobatched", {q}));
   if (!sparse) return fail(SKV_E_NULL, "sparse source is NULL");
   if (sparse->kind != SKV_SRC_PAGED)
     return fail(SKV_E_UNSUPPORTED, "attend_cobatched reads the union of the selections from a paged source");
@@ -663,23 +757,19 @@ skv_status sparsekv_decode_step(const skv_problem* pr, const skv_step_inputs* in
   const skv_problem& p = *pr;
   SKV_TRY(check_step_io(p, in, out));
   const Plan pl = make_plan(p);
+  if (p.pool_location == SKV_POOL_HOST || !pl.fused_step) SKV_TRY(check_select_lds(p, pl));
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);
-  if (p.pool_location == SKV_POOL_DEVICE) {
-    if (pl.fused_step) return enqueue_step(p, pl, *in, *out, ws, s);
-    SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
-    return enqueue_attend_paged(p, pl, *in, *out, ws, s);
-  }
-  if (!k_stage || !v_stage) return fail(SKV_E_NULL, "host pools need staging buffers");
-  if (p.kv_dtype == SKV_FP8_E4M3FN && (!k_stage_scales || !v_stage_scales))
-    return fail(SKV_E_NULL, "fp8 staging needs scale buffers");
+  if (p.pool_location == SKV_POOL_DEVICE) return enqueue_device_step(p, pl, *in, *out, ws, s, 0);
+  HostLayer hl;
+  SKV_TRY(prepare_host_layer(p, pl, *in, *out, k_stage, v_stage, k_stage_scales, v_stage_scales, ws, &hl));
   hipStream_t cs = copy_stream ? as_stream(copy_stream) : s;
   EventSet ev;
   SKV_TRY_HIP(ev.make(2), "event create");
   SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
-  return enqueue_host_layer(p, pl, *in, *out, k_stage, v_stage, k_stage_scales, v_stage_scales, ws,
-                            s, cs, ev.e[0], ev.e[1], nullptr);
+  SKV_TRY_HIP(hipEventRecord(ev.e[0], s), "event record");
+  return enqueue_host_layer(hl, s, cs, ev.e[0], ev.e[1], nullptr);
 }
 
 namespace {
@@ -743,10 +833,34 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
   if (p.window > 0 && p.window % p.block_size != 0)
     return fail(SKV_E_SHAPE, "hybrid step: window buffers need window %% block_size == 0");
   const Plan pl = make_plan(p);
+  SKV_TRY(check_select_lds(p, pl));
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = as_stream(stream);
   const int D = p.head_dim;
+
+  // ---- checks and lookups before any GPU work: the window attention's
+  // arguments and the device addresses of the host part's pinned outputs
+  float* o_win = reinterpret_cast<float*>(ws + pl.off_hybrid);
+  float* lse_win = o_win + (size_t)p.batch * p.n_q_heads * D;
+  AttnParams a{};
+  if (p.window > 0) {
+    a = attn_params(p, pl, in->q, in->seq_lens, o_win, lse_win, ws);
+    skv_kv_source win{SKV_SRC_WINDOW, in->window_k, in->window_v, nullptr, nullptr, nullptr};
+    SKV_TRY(set_source(p, a, &win, false));
+    // no sparse item is attended; waves without an item read row 0 of the window buffers
+    skv_kv_source none{SKV_SRC_STAGED, in->window_k, in->window_v, nullptr, nullptr, nullptr};
+    SKV_TRY(set_source(p, a, &none, true));
+    a.indices = out->indices;
+    a.n_sel = out->n_sel;
+    a.window_only = 1;
+  }
+  float* o_host = nullptr;
+  float* lse_host = nullptr;
+  SKV_TRY_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&o_host), host->o, 0), "host output address");
+  SKV_TRY_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&lse_host), host->lse, 0), "host lse address");
+  EventSet ev;
+  SKV_TRY_HIP(ev.make(1), "event create");
 
   // ---- GPU: scoring and selection, then the inputs of the sparse part to the host
   SKV_TRY(enqueue_score_select(p, pl, *in, *out, ws, s));
@@ -764,40 +878,47 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
     SKV_TRY_HIP(d2h(host->k_scales, in->k_scales, (size_t)p.n_pool_blocks * p.n_kv_heads * 4), "scale copy");
     SKV_TRY_HIP(d2h(host->v_scales, in->v_scales, (size_t)p.n_pool_blocks * p.n_kv_heads * 4), "scale copy");
   }
-  EventSet ev;
-  SKV_TRY_HIP(ev.make(1), "event create");
   SKV_TRY_HIP(hipEventRecord(ev.e[0], s), "event record");
 
   // ---- GPU: attention over the window alone, while the host works
-  float* o_win = reinterpret_cast<float*>(ws + pl.off_hybrid);
-  float* lse_win = o_win + (size_t)p.batch * p.n_q_heads * D;
-  if (p.window > 0) {
-    AttnParams a = attn_params(p, pl, in->q, in->seq_lens, o_win, lse_win, ws);
-    skv_kv_source win{SKV_SRC_WINDOW, in->window_k, in->window_v, nullptr, nullptr, nullptr};
-    SKV_TRY(set_source(p, a, &win, false));
-    // no sparse item is attended; waves without an item read row 0 of the window buffers
-    skv_kv_source none{SKV_SRC_STAGED, in->window_k, in->window_v, nullptr, nullptr, nullptr};
-    SKV_TRY(set_source(p, a, &none, true));
-    a.indices = out->indices;
-    a.n_sel = out->n_sel;
-    a.window_only = 1;
-    SKV_TRY_HIP(launch_attend(a, s), "window attention launch");
-  }
+  if (p.window > 0) SKV_TRY_HIP(launch_attend(a, s), "window attention launch");
 
   // ---- host: the sparse part, once the selection has arrived
   SKV_TRY_HIP(hipEventSynchronize(ev.e[0]), "selection wait");
   host_sparse_attention(host_args(p, *host));
 
   // ---- GPU: fuse the two parts
-  float* o_host = nullptr;
-  float* lse_host = nullptr;
-  SKV_TRY_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&o_host), host->o, 0), "host output address");
-  SKV_TRY_HIP(hipHostGetDevicePointer(reinterpret_cast<void**>(&lse_host), host->lse, 0), "host lse address");
   SKV_TRY_HIP(launch_lse_merge(p.window > 0 ? o_win : nullptr, p.window > 0 ? lse_win : nullptr, o_host, lse_host,
                                out->out, out->lse, p.batch * p.n_q_heads, D, s),
               "fusion launch");
   return SKV_OK;
 }
+
+namespace {
+constexpr int kMaxLayers = 16;
+
+skv_status check_layers(const skv_problem& p, int32_t n_layers, const skv_step_inputs* in,
+                        const skv_step_outputs* out, const char* where) {
+  if (p.pool_location != SKV_POOL_HOST) return fail(SKV_E_UNSUPPORTED, "%s pipelines host pools only", where);
+  if (n_layers < 1 || n_layers > kMaxLayers)
+    return fail(SKV_E_SHAPE, "%s: n_layers %d not in [1, %d]", where, n_layers, kMaxLayers);
+  if (!in || !out) return fail(SKV_E_NULL, "%s: NULL argument", where);
+  for (int l = 0; l < n_layers; ++l) SKV_TRY(check_step_io(p, &in[l], &out[l]));
+  return SKV_OK;
+}
+
+skv_status check_slots(const skv_problem& p, int32_t n_layers, void* const* k, void* const* v,
+                       float* const* ks, float* const* vs, const char* what) {
+  if (!k || !v) return fail(SKV_E_NULL, "%s: NULL slot array", what);
+  for (int slot = 0; slot < 2 && slot < n_layers; ++slot) {
+    if (!k[slot] || !v[slot]) return fail(SKV_E_NULL, "%s slot %d is NULL", what, slot);
+    if (p.kv_dtype == SKV_FP8_E4M3FN && (!ks || !vs || !ks[slot] || !vs[slot]))
+      return fail(SKV_E_NULL, "fp8 %s slot %d needs scales", what, slot);
+    SKV_TRY(check_align16(what, {k[slot], v[slot]}));
+  }
+  return SKV_OK;
+}
+}  // namespace
 
 skv_status sparsekv_decode_layers(const skv_problem* pr, int32_t n_layers, const skv_step_inputs* in,
                                   const skv_step_outputs* out, void* const* k_stage,
@@ -806,20 +927,19 @@ skv_status sparsekv_decode_layers(const skv_problem* pr, int32_t n_layers, const
                                   size_t workspace_bytes, void* stream, void* copy_stream) {
   SKV_TRY(check_problem(pr));
   const skv_problem& p = *pr;
-  if (p.pool_location != SKV_POOL_HOST)
-    return fail(SKV_E_UNSUPPORTED, "decode_layers pipelines host pools only");
-  if (n_layers < 1 || n_layers > 16) return fail(SKV_E_SHAPE, "n_layers %d not in [1, 16]", n_layers);
-  if (!in || !out || !k_stage || !v_stage) return fail(SKV_E_NULL, "decode_layers: NULL argument");
-  for (int l = 0; l < n_layers; ++l) SKV_TRY(check_step_io(p, &in[l], &out[l]));
-  for (int slot = 0; slot < 2 && slot < n_layers; ++slot) {
-    if (!k_stage[slot] || !v_stage[slot]) return fail(SKV_E_NULL, "staging slot %d is NULL", slot);
-    if (p.kv_dtype == SKV_FP8_E4M3FN &&
-        (!k_stage_scales || !v_stage_scales || !k_stage_scales[slot] || !v_stage_scales[slot]))
-      return fail(SKV_E_NULL, "fp8 staging slot %d needs scales", slot);
-  }
+  SKV_TRY(check_layers(p, n_layers, in, out, "decode_layers"));
+  SKV_TRY(check_slots(p, n_layers, k_stage, v_stage, k_stage_scales, v_stage_scales, "staging"));
   const Plan pl = make_plan(p);
+  SKV_TRY(check_select_lds(p, pl));
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
   char* ws = static_cast<char*>(workspace);
+  HostLayer layers[kMaxLayers];
+  for (int l = 0; l < n_layers; ++l) {
+    const int slot = l & 1;
+    SKV_TRY(prepare_host_layer(p, pl, in[l], out[l], k_stage[slot], v_stage[slot],
+                               k_stage_scales ? k_stage_scales[slot] : nullptr,
+                               v_stage_scales ? v_stage_scales[slot] : nullptr, ws, &layers[l]));
+  }
   hipStream_t s = as_stream(stream);
   hipStream_t cs = copy_stream ? as_stream(copy_stream) : s;
   EventSet ev;
@@ -827,42 +947,112 @@ skv_status sparsekv_decode_layers(const skv_problem* pr, int32_t n_layers, const
   hipEvent_t* ev_sel = ev.e;
   hipEvent_t* ev_gather = ev.e + n_layers;
   hipEvent_t* ev_attn = ev.e + 2 * n_layers;
-  // Selection of every layer first (the per-layer queries are given up front,
-  // standing in for the predicted indices of a lookahead scheme), so the copy
-  // stream can run ahead; slot l % 2 is reused once layer l-2's attention is done.
+  // Selection of every layer first (the per-layer queries are given up front),
+  // so the copy stream can run ahead; slot l % 2 is reused once layer l-2's
+  // attention is done.
   for (int l = 0; l < n_layers; ++l) {
     SKV_TRY(enqueue_score_select(p, pl, in[l], out[l], ws, s));
     SKV_TRY_HIP(hipEventRecord(ev_sel[l], s), "event record");
   }
   for (int l = 0; l < n_layers; ++l) {
-    const int slot = l & 1;
-    SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_sel[l], 0), "stream wait");
-    if (l >= 2) SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_attn[l - 2], 0), "stream wait");
-    GatherParams gp = gather_params(p, in[l].k_pool, in[l].v_pool, in[l].k_scales, in[l].v_scales,
-                                    in[l].block_table, out[l].indices, out[l].n_sel, k_stage[slot],
-                                    v_stage[slot], k_stage_scales ? k_stage_scales[slot] : nullptr,
-                                    v_stage_scales ? v_stage_scales[slot] : nullptr);
-    SKV_TRY_HIP(launch_gather(gp, cs), "gather launch");
-    SKV_TRY_HIP(hipEventRecord(ev_gather[l], cs), "event record");
-    SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather[l], 0), "stream wait");
-    AttnParams a = attn_params(p, pl, in[l].q, in[l].seq_lens, out[l].out, out[l].lse, ws);
-    skv_kv_source sparse{SKV_SRC_STAGED, k_stage[slot], v_stage[slot],
-                         k_stage_scales ? k_stage_scales[slot] : nullptr,
-                         v_stage_scales ? v_stage_scales[slot] : nullptr, nullptr};
-    SKV_TRY(set_source(p, a, &sparse, true));
-    if (p.window > 0) {
-      skv_kv_source win{SKV_SRC_WINDOW, in[l].window_k, in[l].window_v, nullptr, nullptr, nullptr};
-      SKV_TRY(set_source(p, a, &win, false));
-    } else {
-      a.window_kind = SKV_SRC_WINDOW;
-    }
-    a.indices = out[l].indices;
-    a.n_sel = out[l].n_sel;
-    SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+    SKV_TRY(enqueue_host_layer(layers[l], s, cs, ev_sel[l], ev_gather[l], l >= 2 ? ev_attn[l - 2] : nullptr));
     SKV_TRY_HIP(hipEventRecord(ev_attn[l], s), "event record");
   }
   // the caller's stream ends after every layer's attention; join the copy stream too
   if (cs != s) SKV_TRY_HIP(hipStreamWaitEvent(s, ev_gather[n_layers - 1], 0), "stream wait");
+  return SKV_OK;
+}
+
+skv_status sparsekv_decode_layers_predicted(const skv_problem* pr, int32_t n_layers,
+                                            const skv_step_inputs* in, const skv_step_outputs* out,
+                                            const skv_layer_prediction* pred, void* const* pref_k,
+                                            void* const* pref_v, float* const* pref_k_scales,
+                                            float* const* pref_v_scales, void* k_stage, void* v_stage,
+                                            float* k_stage_scales, float* v_stage_scales, void* workspace,
+                                            size_t workspace_bytes, void* stream, void* copy_stream) {
+  SKV_TRY(check_problem(pr));
+  const skv_problem& p = *pr;
+  SKV_TRY(check_layers(p, n_layers, in, out, "decode_layers_predicted"));
+  if (!pred) return fail(SKV_E_NULL, "decode_layers_predicted: NULL prediction array");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!pred[l].indices || !pred[l].n_sel) return fail(SKV_E_NULL, "prediction of layer %d is NULL", l);
+    if (pred[l].token < 0 || pred[l].token >= p.n_q_tokens)
+      return fail(SKV_E_SHAPE, "prediction of layer %d: token %d not in [0, %d)", l, pred[l].token,
+                  p.n_q_tokens);
+  }
+  SKV_TRY(check_slots(p, n_layers, pref_k, pref_v, pref_k_scales, pref_v_scales, "prefetch"));
+  const Plan pl = make_plan(p);
+  SKV_TRY(check_select_lds(p, pl));
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  char* ws = static_cast<char*>(workspace);
+  // the real stage must not overlap a prefetch slot: a hit reads a prefetch
+  // slot while other workgroups write the real stage
+  const size_t stage_bytes = (size_t)p.batch * p.n_kv_heads * p.k_max * p.block_size * p.head_dim *
+                             elem_bytes(p.kv_dtype);
+  auto overlaps = [&](const void* a, const void* b) {
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + stage_bytes && y < x + stage_bytes;
+  };
+  for (int slot = 0; slot < 2 && slot < n_layers; ++slot)
+    if (overlaps(k_stage, pref_k[slot]) || overlaps(v_stage, pref_v[slot]) || overlaps(k_stage, pref_v[slot]) ||
+        overlaps(v_stage, pref_k[slot]))
+      return fail(SKV_E_SHAPE, "decode_layers_predicted: the stage overlaps prefetch slot %d", slot);
+  // per layer: the prefetch gather (prediction -> slot l % 2), the correction
+  // (slot -> stage, misses from the pool) and the attention of the stage
+  GatherParams prefetch[kMaxLayers];
+  HostLayer layers[kMaxLayers];
+  for (int l = 0; l < n_layers; ++l) {
+    const int slot = l & 1;
+    float* pks = pref_k_scales ? pref_k_scales[slot] : nullptr;
+    float* pvs = pref_v_scales ? pref_v_scales[slot] : nullptr;
+    prefetch[l] = gather_params(p, in[l].k_pool, in[l].v_pool, in[l].k_scales, in[l].v_scales,
+                                in[l].block_table, pred[l].indices, pred[l].n_sel, pref_k[slot], pref_v[slot],
+                                pks, pvs);
+    prefetch[l].token = pred[l].token;
+    SKV_TRY(prepare_host_layer(p, pl, in[l], out[l], k_stage, v_stage, k_stage_scales, v_stage_scales, ws,
+                               &layers[l]));
+    GatherParams& gp = layers[l].gp;
+    gp.spec_indices = pred[l].indices;
+    gp.spec_n_sel = pred[l].n_sel;
+    gp.spec_token = pred[l].token;
+    gp.spec_k_stage = pref_k[slot];
+    gp.spec_v_stage = pref_v[slot];
+    gp.spec_k_scales = pks;
+    gp.spec_v_scales = pvs;
+    gp.misses = pred[l].misses;
+  }
+  hipStream_t s = as_stream(stream);
+  hipStream_t cs = copy_stream ? as_stream(copy_stream) : s;
+  EventSet ev;
+  SKV_TRY_HIP(ev.make(2 * n_layers + 1), "event create");
+  hipEvent_t* ev_pref = ev.e;
+  hipEvent_t* ev_corr = ev.e + n_layers;
+  hipEvent_t ev_start = ev.e[2 * n_layers];
+  // the copy stream starts after the work the caller queued on `stream`
+  // (which may still be writing the predictions)
+  SKV_TRY_HIP(hipEventRecord(ev_start, s), "event record");
+  SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_start, 0), "stream wait");
+  // copy stream: every layer's predicted blocks, two layers ahead at most
+  // (slot l % 2 is free once layer l-2's correction has read it)
+  auto enqueue_prefetch = [&](int l) -> skv_status {
+    if (l >= 2) SKV_TRY_HIP(hipStreamWaitEvent(cs, ev_corr[l - 2], 0), "stream wait");
+    SKV_TRY_HIP(launch_gather(prefetch[l], cs), "prefetch launch");
+    SKV_TRY_HIP(hipEventRecord(ev_pref[l], cs), "event record");
+    return SKV_OK;
+  };
+  for (int l = 0; l < n_layers && l < 2; ++l) SKV_TRY(enqueue_prefetch(l));
+  // compute stream, per layer in order: selection, then (once the layer's
+  // prefetch is staged) the correction that fetches only the misses, then
+  // the attention of the corrected stage
+  for (int l = 0; l < n_layers; ++l) {
+    SKV_TRY(enqueue_score_select(p, pl, in[l], out[l], ws, s));
+    SKV_TRY_HIP(hipStreamWaitEvent(s, ev_pref[l], 0), "stream wait");
+    SKV_TRY_HIP(launch_gather(layers[l].gp, s), "correction launch");
+    SKV_TRY_HIP(hipEventRecord(ev_corr[l], s), "event record");
+    SKV_TRY_HIP(launch_attend(layers[l].a, s), "attention launch");
+    if (l + 2 < n_layers) SKV_TRY(enqueue_prefetch(l + 2));
+  }
   return SKV_OK;
 }
 

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
         }
       },
       &s_late_next);
-  attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag, nullptr);
+  attend_finish<KV, D, BLK, kPairWaves>(a, smem, b, g, 0, 1, &s_flag);
 
   // ---- the selection's outputs: ids (-1 past the count), counts, overlap
   // (every wave has passed the combine barriers, so both tokens' ids are in LDS)

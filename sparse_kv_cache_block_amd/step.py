@@ -66,31 +66,95 @@ class DecodeStep:
         B.sparsekv_decode_step(self.pr, self.inputs, self.outputs, self.ws, ks, vs, kss, vss,
                                stream=stream, copy_stream=copy_stream)
 
-    def layer_outputs(self, n_layers: int) -> list:
-        """Per-layer output buffers (indices, n_sel, out, lse) for run_layers."""
-        if len(getattr(self, "_layer_bufs", [])) != n_layers:
-            self._layer_bufs = []
-            for _ in range(n_layers):
-                bufs = dict(indices=torch.empty_like(self.indices), n_sel=torch.empty_like(self.n_sel),
-                            out=torch.empty_like(self.out), lse=torch.empty_like(self.lse),
-                            overlap=None if self.overlap is None else torch.empty_like(self.overlap))
-                bufs["struct"] = B.step_outputs(bufs["indices"], bufs["n_sel"], bufs["out"],
-                                                bufs["lse"], bufs["overlap"])
-                self._layer_bufs.append(bufs)
-        return self._layer_bufs
-
     def run_hybrid(self, host: "HybridHost", stream=None) -> None:
         """Host pool: the hybrid step (window on the GPU, selected blocks on the host)."""
         B.sparsekv_decode_step_hybrid(self.pr, self.inputs, self.outputs, host.part, self.ws, stream)
 
-    def run_layers(self, n_layers: int, stream=None, copy_stream=None) -> list:
-        """Host pool: n_layers layer-steps over the same inputs through the
-        two-slot staging pipeline; returns the per-layer output buffers."""
-        outs = self.layer_outputs(n_layers)
-        B.sparsekv_decode_layers(self.pr, [self.inputs] * n_layers, [o["struct"] for o in outs],
-                                 self.k_stage, self.v_stage, self.ws, self.k_stage_scales,
-                                 self.v_stage_scales, stream=stream, copy_stream=copy_stream)
-        return outs
+
+def _stage_slots(inp: DecodeInputs, km: int, n: int, device) -> tuple:
+    """n staging buffers [B][Hkv][k_max][blk][d] for K and V (and fp8 scales)."""
+    wl = inp.wl
+    shape = (wl.batch, wl.n_kv_heads, km, wl.block_size, wl.head_dim)
+    k = [torch.empty(shape, dtype=inp.k_pool.dtype, device=device) for _ in range(n)]
+    v = [torch.empty(shape, dtype=inp.v_pool.dtype, device=device) for _ in range(n)]
+    ks = vs = None
+    if inp.k_scales is not None:
+        ks = [torch.empty(shape[:3], dtype=torch.float32, device=device) for _ in range(n)]
+        vs = [torch.empty(shape[:3], dtype=torch.float32, device=device) for _ in range(n)]
+    return k, v, ks, vs
+
+
+class LayerPipeline:
+    """The host-pool layer pipelines over one input set per layer (each with
+    its own query, landmarks, pinned pool, table and window, all of one
+    problem shape): per-layer outputs, one shared workspace, two staging slots
+    and, for the predicted pipeline, the stage the correction writes.
+    Allocation and forwarding only."""
+
+    def __init__(self, layers: list, k_max: Optional[int] = None, device="cuda"):
+        self.layers = layers
+        self.pr = problem_for(layers[0], k_max)
+        for inp in layers[1:]:
+            other = problem_for(inp, k_max)
+            for f, _ in B.Problem._fields_:
+                if getattr(other, f) != getattr(self.pr, f):
+                    raise ValueError(f"layer inputs differ in problem field {f}")
+        wl = layers[0].wl
+        km = self.pr.k_max
+        Bn, T, Hq, Hkv, d = wl.batch, wl.n_q_tokens, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+        self.device = device
+        self.ws = B.alloc_workspace(self.pr, device)
+        self.outs = []
+        for _ in layers:
+            o = dict(indices=torch.empty((Bn, T, Hkv, km), dtype=torch.int32, device=device),
+                     n_sel=torch.empty((Bn, T, Hkv), dtype=torch.int32, device=device),
+                     out=torch.empty((Bn, Hq, d), dtype=torch.float32, device=device),
+                     lse=torch.empty((Bn, Hq), dtype=torch.float32, device=device),
+                     overlap=torch.empty((Bn, Hkv), dtype=torch.float32, device=device) if T == 2 else None,
+                     misses=torch.empty((Bn, Hkv), dtype=torch.int32, device=device))
+            o["struct"] = B.step_outputs(o["indices"], o["n_sel"], o["out"], o["lse"], o["overlap"])
+            self.outs.append(o)
+        self.inputs = [B.step_inputs(inp.q, inp.landmarks, inp.k_pool, inp.v_pool, inp.k_scales, inp.v_scales,
+                                     inp.block_table, inp.seq_lens, inp.k_per_seq, inp.window_k, inp.window_v)
+                       for inp in layers]
+        self.k_slots, self.v_slots, self.k_slot_scales, self.v_slot_scales = _stage_slots(layers[0], km, 2, device)
+        self.stage = None
+
+    def staging_buffers(self) -> list:
+        """Every staging tensor the pipelines write (slots, then the predicted stage)."""
+        bufs = list(self.k_slots) + list(self.v_slots)
+        for extra in (self.k_slot_scales, self.v_slot_scales):
+            bufs += list(extra or [])
+        if self.stage is not None:
+            bufs += [t for t in self.stage if t is not None]
+        return bufs
+
+    def run(self, stream=None, copy_stream=None) -> list:
+        """sparsekv_decode_layers: every layer's selection, then gathers into
+        slot l % 2 on the copy stream and attention on `stream`."""
+        B.sparsekv_decode_layers(self.pr, self.inputs, [o["struct"] for o in self.outs], self.k_slots,
+                                 self.v_slots, self.ws, self.k_slot_scales, self.v_slot_scales,
+                                 stream=stream, copy_stream=copy_stream)
+        return self.outs
+
+    def alloc_stage(self) -> None:
+        """The stage the predicted pipeline's corrections write (allocated once)."""
+        if self.stage is None:
+            k, v, ks, vs = _stage_slots(self.layers[0], self.pr.k_max, 1, self.device)
+            self.stage = (k[0], v[0], ks[0] if ks else None, vs[0] if vs else None)
+
+    def run_predicted(self, predictions: list, stream=None, copy_stream=None) -> list:
+        """sparsekv_decode_layers_predicted.  predictions[l] = (indices, n_sel,
+        token): layer l's predicted selection (row `token` of an earlier
+        selection); the per-layer miss counts land in outs[l]["misses"]."""
+        self.alloc_stage()
+        preds = [B.layer_prediction(idx, nsel, tok, o["misses"])
+                 for (idx, nsel, tok), o in zip(predictions, self.outs)]
+        k, v, ks, vs = self.stage
+        B.sparsekv_decode_layers_predicted(self.pr, self.inputs, [o["struct"] for o in self.outs], preds,
+                                           self.k_slots, self.v_slots, k, v, self.ws, self.k_slot_scales,
+                                           self.v_slot_scales, ks, vs, stream=stream, copy_stream=copy_stream)
+        return self.outs
 
 
 def device_pointer_of_pinned(t: torch.Tensor) -> int:

@@ -220,3 +220,176 @@ def test_stream_read_validates_before_launch(lib):
     assert lib.sparsekv_stream_read(0x1008, 16, 0x1000, 4, None) == B.SKV_E_SHAPE
     assert lib.sparsekv_stream_read(0x1000, 16, 0x1000, 2, None) == B.SKV_E_SHAPE
     assert len(B.sparsekv_last_error()) > 0
+
+
+# ---------------------------------------------------------------- LDS limits
+# The selection keeps a pair's keys in one workgroup's 160 KiB of LDS; shapes
+# beyond it fail with SKV_E_UNSUPPORTED before any launch.  Each case probes
+# both sides of the limit: just inside it, the call gets past the LDS check
+# and stops at the (too small) workspace or at a NULL pointer instead.
+D = 0x1000
+
+
+def _step_args():
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, None, None)
+    outs = B.StepOutputs(D, D, D, D, D)
+    return ins, outs
+
+
+def _decode_step(lib, pr, ws_bytes=16):
+    ins, outs = _step_args()
+    return lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), D, D, None, None, D, ws_bytes,
+                                    None, None)
+
+
+def _limit_problem(T, k_max, B_=1, **kw):
+    # 16384 blocks of 64 tokens, window 256: 16380 candidates per sequence
+    base = dict(B=B_, T=T, Hq=32, Hkv=8, blk=64, max_blocks=16384, n_pool_blocks=16384 * B_,
+                stride_block=8 * 64 * 128, stride_head=64 * 128, window=256, k_max=k_max)
+    base.update(kw)
+    return _good_problem(**base)
+
+
+@pytest.mark.parametrize("T,k_ok,k_bad", [(2, 3187, 3188), (1, 11441, 11442)])
+def test_selection_lds_limit_two_launch_step(lib, T, k_ok, k_bad):
+    # 8 pairs: the two-launch step, whose scoring workgroups select
+    assert _decode_step(lib, _limit_problem(T, k_ok)) == B.SKV_E_WORKSPACE
+    assert _decode_step(lib, _limit_problem(T, k_bad)) == B.SKV_E_UNSUPPORTED
+    assert "LDS" in B.sparsekv_last_error()
+
+
+def test_selection_lds_limit_many_pairs(lib):
+    # T = 2 with 16380 candidates and k_max 4096 at 256 pairs: too big for the
+    # single-launch step, and its two-launch selection does not fit either
+    pr = _limit_problem(2, 4096, B_=32)
+    assert B.sparsekv_decode_step_launches(pr) == 2
+    assert _decode_step(lib, pr) == B.SKV_E_UNSUPPORTED
+    # the single-launch step keeps its own LDS check: a fitting shape plans
+    assert B.sparsekv_decode_step_launches(_limit_problem(1, 64, B_=32, blk=32, max_blocks=1024,
+                                                          stride_block=8 * 32 * 128, stride_head=32 * 128,
+                                                          window=512)) == 1
+
+
+def test_topk_lds_limit(lib):
+    ok = _good_problem(max_blocks=16384, n_pool_blocks=16384, k_max=11759)
+    bad = _good_problem(max_blocks=16384, n_pool_blocks=16384, k_max=11760)
+    # inside the limit the call reaches the pointer checks; beyond it, it stops first
+    assert lib.sparsekv_topk(C.byref(ok), D, D, D, None, D, None, None) == B.SKV_E_NULL
+    assert lib.sparsekv_topk(C.byref(bad), D, D, D, None, D, None, None) == B.SKV_E_UNSUPPORTED
+    bad12k = _good_problem(max_blocks=16384, n_pool_blocks=16384, k_max=12000)
+    assert lib.sparsekv_topk(C.byref(bad12k), D, D, D, D, D, None, None) == B.SKV_E_UNSUPPORTED
+
+
+def test_hybrid_and_layers_check_selection_lds(lib):
+    pr = _limit_problem(2, 4096)
+    pr.pool_location = B.SKV_POOL_HOST
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D)
+    outs = B.StepOutputs(D, D, D, D, D)
+    host = B.HostPart(D, D, 0, D, D, D, D, D, None, None, D, D)
+    assert lib.sparsekv_decode_step_hybrid(C.byref(pr), C.byref(ins), C.byref(outs), C.byref(host), D, 16,
+                                           None) == B.SKV_E_UNSUPPORTED
+    slots = (C.c_void_p * 2)(D, D)
+    assert lib.sparsekv_decode_layers(C.byref(pr), 1, C.byref(ins), C.byref(outs), slots, slots, None, None,
+                                      D, 16, None, None) == B.SKV_E_UNSUPPORTED
+
+
+# ------------------------------------------------ host-pool checks before enqueue
+def _host_problem(**kw):
+    base = dict(B=2, T=1, Hq=8, Hkv=2, d=128, blk=32, max_blocks=64, n_pool_blocks=128, window=64, k_max=8,
+                kv_dtype="bf16")
+    base.update(kw)
+    return B.make_problem(base["B"], base["T"], base["Hq"], base["Hkv"], base["d"], base["blk"],
+                          base["max_blocks"], base["n_pool_blocks"], base["blk"] * base["d"],
+                          base["n_pool_blocks"] * base["blk"] * base["d"], base["window"], base["k_max"],
+                          "bf16", base["kv_dtype"], "bf16", pool_location=B.SKV_POOL_HOST)
+
+
+@pytest.mark.parametrize("kw,status,text", [
+    (dict(kv_dtype="fp8"), B.SKV_E_UNSUPPORTED, "fp8 window"),
+    (dict(window=48), B.SKV_E_SHAPE, "window"),
+])
+def test_host_pool_window_checked_before_any_launch(lib, kw, status, text):
+    # the window-source checks run before the scoring launch (dummy pointers:
+    # a launch would fail here with SKV_E_HIP, not with these statuses)
+    pr = _host_problem(**kw)
+    n = B.sparsekv_workspace_size(pr)
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D)
+    outs = B.StepOutputs(D, D, D, D, None)
+    assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), D, D, D, D, D, n, None,
+                                    None) == status
+    assert text in B.sparsekv_last_error()
+    slots = (C.c_void_p * 2)(D, D)
+    ins3 = (B.StepInputs * 3)(ins, ins, ins)
+    outs3 = (B.StepOutputs * 3)(outs, outs, outs)
+    assert lib.sparsekv_decode_layers(C.byref(pr), 3, ins3, outs3, slots, slots, slots, slots, D, n, None,
+                                      None) == status
+    preds = (B.LayerPrediction * 3)(*[B.LayerPrediction(D, D, 0, None)] * 3)
+    assert lib.sparsekv_decode_layers_predicted(C.byref(pr), 3, ins3, outs3, preds, slots, slots, slots, slots,
+                                                0x10000000, 0x20000000, D, D, D, n, None, None) == status
+
+
+def test_host_pool_staging_checked_before_any_launch(lib):
+    pr = _host_problem()
+    n = B.sparsekv_workspace_size(pr)
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D)
+    outs = B.StepOutputs(D, D, D, D, None)
+    assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), None, D, None, None, D, n, None,
+                                    None) == B.SKV_E_NULL
+    assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), 0x1008, D, None, None, D, n,
+                                    None, None) == B.SKV_E_SHAPE
+    assert "aligned" in B.sparsekv_last_error()
+
+
+def test_predicted_layers_validation(lib):
+    pr = _host_problem(T=2)
+    n = B.sparsekv_workspace_size(pr)
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D)
+    outs = B.StepOutputs(D, D, D, D, None)
+    ins2 = (B.StepInputs * 2)(ins, ins)
+    outs2 = (B.StepOutputs * 2)(outs, outs)
+    slots = (C.c_void_p * 2)(0x1000000, 0x2000000)
+
+    def call(preds, stage=0x30000000, problem=pr, ws=n):
+        arr = (B.LayerPrediction * 2)(*preds)
+        return lib.sparsekv_decode_layers_predicted(C.byref(problem), 2, ins2, outs2, arr, slots, slots, None,
+                                                    None, stage, stage, None, None, D, ws, None, None)
+
+    good = B.LayerPrediction(D, D, 1, None)
+    assert call([good, B.LayerPrediction(None, D, 1, None)]) == B.SKV_E_NULL
+    assert call([good, B.LayerPrediction(D, D, 2, None)]) == B.SKV_E_SHAPE
+    # the real stage may not overlap a prefetch slot (a hit reads one while the stage is written)
+    assert call([good, good], stage=0x2000000 + 0x100) == B.SKV_E_SHAPE
+    assert "overlaps" in B.sparsekv_last_error()
+    assert call([good, good], ws=16) == B.SKV_E_WORKSPACE
+    dev = _good_problem(T=2)
+    assert call([good, good], problem=dev) == B.SKV_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- alignment
+def test_pool_strides_must_be_16_byte_multiples(lib):
+    # bf16 elements: a stride of 4 elements is 8 bytes
+    n = C.c_size_t(0)
+    pr = _good_problem(stride_block=2 * 32 * 128 + 4)
+    assert lib.sparsekv_workspace_size(C.byref(pr), C.byref(n)) == B.SKV_E_SHAPE
+    pr = _good_problem(kv_dtype="fp8", stride_head=32 * 128 + 8)
+    assert lib.sparsekv_workspace_size(C.byref(pr), C.byref(n)) == B.SKV_E_SHAPE
+    assert lib.sparsekv_workspace_size(C.byref(_good_problem(kv_dtype="fp8", stride_head=32 * 128 + 16)),
+                                       C.byref(n)) == B.SKV_OK
+
+
+def test_vector_buffers_must_be_16_byte_aligned(lib):
+    pr = _good_problem()
+    assert lib.sparsekv_score(C.byref(pr), 0x1008, D, D, D, None) == B.SKV_E_SHAPE
+    assert lib.sparsekv_score(C.byref(pr), D, 0x1004, D, D, None) == B.SKV_E_SHAPE
+    assert lib.sparsekv_gather(C.byref(pr), D, 0x1002, None, None, D, D, D, D, D, None, None, None) == B.SKV_E_SHAPE
+    n = B.sparsekv_workspace_size(pr)
+    src = B.KvSource(B.SKV_SRC_PAGED, 0x1010, 0x1008, None, None, D)
+    ok = B.KvSource(B.SKV_SRC_PAGED, D, D, None, None, D)
+    assert lib.sparsekv_attend(C.byref(pr), D, C.byref(src), D, D, C.byref(ok), D, D, None, D, n,
+                               None) == B.SKV_E_SHAPE
+    assert lib.sparsekv_attend(C.byref(pr), 0x1001, C.byref(ok), D, D, C.byref(ok), D, D, None, D, n,
+                               None) == B.SKV_E_SHAPE
+    ins = B.StepInputs(D, D, 0x1004, D, None, None, D, D, D, None, None)
+    outs = B.StepOutputs(D, D, D, D, None)
+    assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), None, None, None, None, D, n,
+                                    None, None) == B.SKV_E_SHAPE

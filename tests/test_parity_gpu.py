@@ -580,39 +580,210 @@ def test_hybrid_step_full_host_workload():
     check_hybrid(configs.HOST)
 
 
-def test_host_layer_pipeline_matches_single_steps():
-    wl = configs.HOST.scaled(batch=2, context=8192)
-    announce("sparsekv_decode_layers (ping-pong, 4 layers) vs single steps")
-    inp, st = run_step(wl)
-    outs = st.run_layers(4, copy_stream=torch.cuda.Stream())
+# ------------------------------------------------ host-pool layer pipelines
+# Every layer gets its own input set (query, pinned pool, landmarks, table and
+# window of another instance), so layers select different blocks and stage
+# different bytes.  Both staging slots (and the predicted pipeline's stage) are
+# filled with NaN before every call: a gather that ran late, a slot mix-up or
+# an attention that did not wait for its gather reads NaN or another layer's
+# blocks, and fails the per-layer comparison with the oracle.
+_LAYER_INPUTS = {}
+
+
+def layer_inputs(wl, n_layers):
+    """Host copies and device placements of n_layers independent input sets."""
+    key = (wl, n_layers)
+    if key not in _LAYER_INPUTS:
+        _LAYER_INPUTS.clear()
+        host = [make_inputs(wl, device="cpu", instance=l) for l in range(n_layers)]
+        _LAYER_INPUTS[key] = (host, [to_device_for(h) for h in host])
+    return _LAYER_INPUTS[key]
+
+
+def poison(tensors):
+    """Fill with NaN: bf16 0x7FC0, fp8 e4m3fn 0x7F, fp32 NaN."""
+    for t in tensors:
+        if t.dtype == torch.bfloat16:
+            t.view(torch.int16).fill_(0x7FC0)
+        elif t.element_size() == 1:
+            t.view(torch.uint8).fill_(0x7F)
+        else:
+            t.fill_(float("nan"))
+
+
+def check_layers_against_oracle(wl, host, outs):
+    """Each layer's selection, output and lse against the oracle's decode step on
+    that layer's own inputs."""
+    for l, (inp, o) in enumerate(zip(host, outs)):
+        h = HostArrays(inp)
+        orc = O.decode_step(oracle_problem(inp), h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens,
+                            h.k_per_seq)
+        gi, gn = _np(o["indices"]), _np(o["n_sel"])
+        check_indices(gi, gn, orc["indices"], orc["n_sel"], orc["scores"], h.seq_lens, wl.window, wl.block_size)
+        compare_attention(inp, h, gi, gn, _np(o["out"]), _np(o["lse"]), TOL[wl.kv_dtype])
+    # the layers really differ (otherwise a slot mix-up could go unseen)
+    if len(outs) > 1:
+        assert not torch.equal(outs[0]["indices"], outs[1]["indices"])
+        assert not torch.equal(outs[0]["out"], outs[1]["out"])
+
+
+PIPE_WL = configs.HOST.scaled(batch=2, context=8192)
+
+
+@pytest.mark.parametrize("n_layers", [2, 4, 8])
+def test_host_layer_pipeline_per_layer_oracle(n_layers):
+    announce(f"sparsekv_decode_layers, {n_layers} layers with their own inputs, poisoned slots")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(PIPE_WL, 8)
+    pipe = LayerPipeline(dev[:n_layers])
+    poison(pipe.staging_buffers())
+    pipe.run(copy_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
-    for o in outs:
-        assert torch.equal(o["indices"], st.indices)
-        assert torch.equal(o["out"], st.out) and torch.equal(o["lse"], st.lse)
+    check_layers_against_oracle(PIPE_WL, host[:n_layers], pipe.outs)
 
 
-def test_host_pipeline_depth_and_delayed_copy_stream():
-    # two slots for any depth: 2 and 8 layers give the single step's result; and
-    # with the copy stream held up by a long kernel, every layer's attention
-    # still waits for its own gather (the events order them)
-    wl = configs.HOST.scaled(batch=2, context=8192)
-    announce("host ping-pong pipeline: 2 and 8 layers, delayed copy stream")
-    inp, st = run_step(wl)
-    ref = (st.out.clone(), st.lse.clone(), st.indices.clone())
-    for n in (2, 8):
-        outs = st.run_layers(n, copy_stream=torch.cuda.Stream())
-        torch.cuda.synchronize()
-        assert len(outs) == n
-        for o in outs:
-            assert torch.equal(o["indices"], ref[2])
-            assert torch.equal(o["out"], ref[0]) and torch.equal(o["lse"], ref[1])
+def test_host_layer_pipeline_delayed_copy_stream():
+    # the copy stream held up by a bounded spin kernel queued ahead of the
+    # gathers, with NaN in both slots: every attention must still wait for its
+    # own layer's gather (the events order them) and give the undelayed result
+    announce("sparsekv_decode_layers, 5 layers, poisoned slots, delayed copy stream")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(PIPE_WL, 8)
+    pipe = LayerPipeline(dev[:5])
+    poison(pipe.staging_buffers())
+    pipe.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    ref = [(o["out"].clone(), o["lse"].clone(), o["indices"].clone()) for o in pipe.outs]
+    check_layers_against_oracle(PIPE_WL, host[:5], pipe.outs)
+    for o in pipe.outs:
+        o["out"].fill_(0)
+    poison(pipe.staging_buffers())
     cs = torch.cuda.Stream()
     with torch.cuda.stream(cs):
         torch.cuda._sleep(200_000_000)   # a bounded spin kernel, tens of ms
-    outs = st.run_layers(4, copy_stream=cs)
+    pipe.run(copy_stream=cs)
     torch.cuda.synchronize()
-    for o in outs:
-        assert torch.equal(o["out"], ref[0]) and torch.equal(o["lse"], ref[1])
+    for o, (out, lse, idx) in zip(pipe.outs, ref):
+        assert torch.equal(o["indices"], idx)
+        assert torch.equal(o["out"], out) and torch.equal(o["lse"], lse)
+
+
+def test_host_layer_pipeline_fp8_odd_layers():
+    wl = configs.HOST.scaled(batch=2, context=4096, window=0, kv_dtype="fp8")
+    announce("sparsekv_decode_layers, fp8 pool, 3 layers, poisoned slots and stage scales")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(wl, 3)
+    pipe = LayerPipeline(dev)
+    poison(pipe.staging_buffers())
+    pipe.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    check_layers_against_oracle(wl, host, pipe.outs)
+
+
+PRED_WL = configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3)
+
+
+def _expected_misses(real_idx, real_n, pred_idx, pred_n, token):
+    Bn, _, Hkv, _ = real_idx.shape
+    m = np.zeros((Bn, Hkv), dtype=np.int64)
+    for b in range(Bn):
+        for g in range(Hkv):
+            r = set(real_idx[b, 0, g, :real_n[b, 0, g]].tolist())
+            q = set(pred_idx[b, token, g, :pred_n[b, token, g]].tolist())
+            m[b, g] = len(r - q)
+    return m
+
+
+def _run_predicted(pipe, preds, copy_stream):
+    pipe.alloc_stage()
+    poison(pipe.staging_buffers())
+    for o in pipe.outs:
+        o["misses"].fill_(-1)
+        o["out"].fill_(0)
+    pipe.run_predicted(preds, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("kind", ["speculative", "empty", "exact", "other_layer"])
+def test_predicted_layer_pipeline(kind):
+    # The prediction of layer l: the speculative token's selection of a
+    # previous step on the same layer ("speculative"); nothing (every block a
+    # miss); the real selection itself (no miss); another layer's selection
+    # (hits only by chance).  Whatever it is, each layer's stage must hold the
+    # real selection's gather, so results equal the plain pipeline's bit for
+    # bit and the oracle's at the dtype's bound; misses match the set difference.
+    n = 4
+    announce(f"sparsekv_decode_layers_predicted, {n} layers, prediction = {kind}")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(PRED_WL, n)
+    plain = LayerPipeline(dev)
+    poison(plain.staging_buffers())
+    plain.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    check_layers_against_oracle(PRED_WL, host, plain.outs)
+    prev = [(o["indices"].clone(), o["n_sel"].clone()) for o in plain.outs]
+    if kind == "speculative":
+        preds = [(idx, nsel, 1) for idx, nsel in prev]
+    elif kind == "empty":
+        preds = [(idx, torch.zeros_like(nsel), 1) for idx, nsel in prev]
+    elif kind == "exact":
+        preds = [(idx, nsel, 0) for idx, nsel in prev]
+    else:
+        preds = [(prev[(l + 1) % n][0], prev[(l + 1) % n][1], 0) for l in range(n)]
+    pipe = LayerPipeline(dev)
+    _run_predicted(pipe, preds, torch.cuda.Stream())
+    check_layers_against_oracle(PRED_WL, host, pipe.outs)
+    total = 0
+    for l, (o, p) in enumerate(zip(pipe.outs, plain.outs)):
+        assert torch.equal(o["indices"], p["indices"]) and torch.equal(o["n_sel"], p["n_sel"])
+        assert torch.equal(o["out"], p["out"]) and torch.equal(o["lse"], p["lse"])
+        exp = _expected_misses(_np(o["indices"]), _np(o["n_sel"]), _np(preds[l][0]), _np(preds[l][1]), preds[l][2])
+        assert np.array_equal(_np(o["misses"]), exp), (l, _np(o["misses"]), exp)
+        total += int(exp.sum())
+    nsel0 = sum(int(o["n_sel"][:, 0].sum()) for o in pipe.outs)
+    if kind == "empty":
+        assert total == nsel0
+    elif kind == "exact":
+        assert total == 0
+    elif kind == "speculative":
+        assert 0 < total < nsel0
+    print(f"[case] ok: {total} of {nsel0} selected blocks missed", flush=True)
+
+
+def test_predicted_layer_pipeline_delayed_copy_stream():
+    # prefetches held up behind a bounded spin kernel, slots poisoned: each
+    # correction must wait for its layer's prefetch (a hit read early would be NaN)
+    announce("sparsekv_decode_layers_predicted, 5 layers, delayed copy stream, poisoned slots")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(PRED_WL, 5)
+    plain = LayerPipeline(dev)
+    plain.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    preds = [(o["indices"].clone(), o["n_sel"].clone(), 1) for o in plain.outs]
+    pipe = LayerPipeline(dev)
+    cs = torch.cuda.Stream()
+    with torch.cuda.stream(cs):
+        torch.cuda._sleep(200_000_000)
+    _run_predicted(pipe, preds, cs)
+    check_layers_against_oracle(PRED_WL, host, pipe.outs)
+    for o, p in zip(pipe.outs, plain.outs):
+        assert torch.equal(o["out"], p["out"]) and torch.equal(o["lse"], p["lse"])
+
+
+def test_predicted_layer_pipeline_fp8():
+    wl = configs.HOST.scaled(batch=2, context=4096, window=0, kv_dtype="fp8", n_q_tokens=2, spec_noise=0.3)
+    announce("sparsekv_decode_layers_predicted, fp8 pool, 3 layers")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(wl, 3)
+    plain = LayerPipeline(dev)
+    plain.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    preds = [(o["indices"].clone(), o["n_sel"].clone(), 1) for o in plain.outs]
+    pipe = LayerPipeline(dev)
+    _run_predicted(pipe, preds, torch.cuda.Stream())
+    check_layers_against_oracle(wl, host, pipe.outs)
+    for o, p in zip(pipe.outs, plain.outs):
+        assert torch.equal(o["out"], p["out"]) and torch.equal(o["lse"], p["lse"])
 
 
 def test_repeated_calls_reuse_workspace():
