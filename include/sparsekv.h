@@ -317,6 +317,23 @@ skv_status sparsekv_decode_step(const skv_problem *pr, const skv_step_inputs *in
                                 void *stream, void *copy_stream);
 
 /*
+ * sparsekv_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid allocation).  Device pools only (SKV_E_UNSUPPORTED
+ * for a host pool).  The workspace is a fixed array of 32 MiB inside the
+ * library, one per GPU, held until the process ends; a problem whose
+ * sparsekv_workspace_size exceeds it returns SKV_E_WORKSPACE before any GPU
+ * work.  Every call on a GPU uses that GPU's one array: a fill kernel clears
+ * its arrival counters first (no memset node, so the call can be captured),
+ * and calls that overlap in time on one GPU -- on different streams, or from
+ * different threads -- race on it and give undefined results.  The call
+ * itself allocates nothing (its first call on a device looks up the array's
+ * address there).  Results equal sparsekv_decode_step's bit for bit.
+ */
+skv_status sparsekv_decode_step_noalloc(const skv_problem *pr, const skv_step_inputs *in,
+                                        const skv_step_outputs *out, void *stream);
+
+/*
  * Host side of the hybrid step: the pool's host addresses and pinned host
  * buffers the caller owns (allocated with hipHostMalloc or equivalent, so the
  * GPU can read o and lse).  The call fills the buffers below.

@@ -27,7 +27,7 @@ EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
             "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
             "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid", "sparsekv_host_attention",
-            "sparsekv_stream_read", "sparsekv_decode_layers_predicted")
+            "sparsekv_stream_read", "sparsekv_decode_layers_predicted", "sparsekv_decode_step_noalloc")
 
 
 class SkvError(RuntimeError):
@@ -110,6 +110,7 @@ def lib() -> C.CDLL:
             "sparsekv_host_attention": (C.c_int, [P, C.POINTER(HostPart)]),
             "sparsekv_decode_step": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
                                                vp, vp, vp, vp, vp, sz, vp, vp]),
+            "sparsekv_decode_step_noalloc": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs), vp]),
             "sparsekv_decode_layers": (C.c_int, [P, C.c_int32, C.POINTER(StepInputs),
                                                  C.POINTER(StepOutputs), C.POINTER(vp), C.POINTER(vp),
                                                  C.POINTER(vp), C.POINTER(vp), vp, sz, vp, vp]),
@@ -258,6 +259,11 @@ def sparsekv_decode_step(pr: Problem, inputs: StepInputs, outputs: StepOutputs, 
                                       _ptr(v_stage), _ptr(k_stage_scales), _ptr(v_stage_scales),
                                       _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream), cs), "sparsekv_decode_step")
+
+
+def sparsekv_decode_step_noalloc(pr: Problem, inputs: StepInputs, outputs: StepOutputs, stream=None) -> None:
+    _check(lib().sparsekv_decode_step_noalloc(C.byref(pr), C.byref(inputs), C.byref(outputs), _stream(stream)),
+           "sparsekv_decode_step_noalloc")
 
 
 def sparsekv_decode_step_hybrid(pr: Problem, inputs: StepInputs, outputs: StepOutputs, host: HostPart,

@@ -393,3 +393,20 @@ def test_vector_buffers_must_be_16_byte_aligned(lib):
     outs = B.StepOutputs(D, D, D, D, None)
     assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), None, None, None, None, D, n,
                                     None, None) == B.SKV_E_SHAPE
+
+
+def test_noalloc_step_rejects_host_pools_and_oversized_problems(lib):
+    # both checks run on the host before any HIP call
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D)
+    outs = B.StepOutputs(D, D, D, D, None)
+    assert lib.sparsekv_decode_step_noalloc(C.byref(_host_problem()), C.byref(ins), C.byref(outs),
+                                            None) == B.SKV_E_UNSUPPORTED
+    # 512 pairs x 2 tokens x 16380 candidates of score staging: beyond the 32 MiB array
+    big = _limit_problem(2, 16, B_=64, Hq=64)
+    assert B.sparsekv_workspace_size(big) > 32 << 20
+    assert lib.sparsekv_decode_step_noalloc(C.byref(big), C.byref(ins), C.byref(outs), None) == B.SKV_E_WORKSPACE
+    assert "workspace" in B.sparsekv_last_error()
+    # a problem that fits gets past every check (stopped here by a NULL output)
+    no_out = B.StepOutputs(D, D, None, D, None)
+    assert lib.sparsekv_decode_step_noalloc(C.byref(_good_problem()), C.byref(ins), C.byref(no_out),
+                                            None) == B.SKV_E_NULL
