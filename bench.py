@@ -219,6 +219,90 @@ def gather_correct_probe(reps: int) -> int:
     return 0
 
 
+def predicted_layers_probe(reps: int, n_layers: int = 4) -> int:
+    """Host-pool workload with a speculative second query token (real +
+    N(0, 0.3)) over n_layers layer-steps: the plain two-slot pipeline (each
+    layer's selected blocks gathered over the host link after its selection)
+    against the predicted one (each layer's blocks prefetched by the previous
+    step's speculative selection, then only the misses fetched after the real
+    selection).  Reports both pipelines' time per layer and host-link bytes
+    per layer, and the per-layer critical path after a layer's selection: the
+    full gather against the correction of an already staged prediction."""
+    import torch
+
+    from sparse_kv_cache_block_amd import binding as B
+    from sparse_kv_cache_block_amd import configs
+    from sparse_kv_cache_block_amd.inputs import make_inputs
+    from sparse_kv_cache_block_amd.step import LayerPipeline, to_device_for
+
+    wl = configs.HOST.scaled(n_q_tokens=2, spec_noise=0.3)
+    torch.cuda.set_device(0)
+    layers = [to_device_for(make_inputs(wl, device="cuda", instance=l)) for l in range(n_layers)]
+    pipe = LayerPipeline(layers)
+    cs = torch.cuda.Stream()
+    pipe.run(copy_stream=cs)
+    torch.cuda.synchronize()
+    # the previous step's selections: the speculative token's rows predict this step's
+    preds = [(o["indices"].clone(), o["n_sel"].clone(), 1) for o in pipe.outs]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn) -> float:
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        ev[1].synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / reps
+
+    t_plain = timed(lambda: pipe.run(copy_stream=cs))
+    t_pred = timed(lambda: pipe.run_predicted(preds, copy_stream=cs))
+    chunk = 2 * wl.block_size * wl.head_dim * configs.ELEM_BYTES[wl.kv_dtype]
+    real = sum(int(o["n_sel"][:, 0].sum()) for o in pipe.outs)
+    pref = sum(int(p[1][:, 1].sum()) for p in preds)
+    miss = sum(int(o["misses"].sum()) for o in pipe.outs)
+
+    # critical path of one layer after its selection: gather + attention
+    # (plain) against correction + attention (predicted, prefetch staged)
+    st_in, o0 = layers[0], pipe.outs[0]
+    pools = (st_in.k_pool, st_in.v_pool, st_in.k_scales, st_in.v_scales, st_in.block_table)
+    pk, pv = pipe.k_slots[0], pipe.v_slots[0]
+    k_st, v_st = pipe.stage[0], pipe.stage[1]
+    B.sparsekv_gather(pipe.pr, *pools, preds[0][0][:, 1:], preds[0][1][:, 1:], pk, pv, None, None)
+    sp = B.kv_source(B.SKV_SRC_STAGED, k_st, v_st)
+    win = B.kv_source(B.SKV_SRC_WINDOW, st_in.window_k, st_in.window_v)
+    out = torch.empty_like(o0["out"])
+    lse = torch.empty_like(o0["lse"])
+
+    def plain_path():
+        B.sparsekv_gather(pipe.pr, *pools, o0["indices"], o0["n_sel"], k_st, v_st, None, None)
+        B.sparsekv_attend(pipe.pr, st_in.q, sp, o0["indices"], o0["n_sel"], win, st_in.seq_lens, out, lse, pipe.ws)
+
+    def pred_path():
+        B.sparsekv_gather_correct(pipe.pr, *pools, preds[0][0], preds[0][1], 1, pk, pv, None, None,
+                                  o0["indices"], o0["n_sel"], 0, k_st, v_st)
+        B.sparsekv_attend(pipe.pr, st_in.q, sp, o0["indices"], o0["n_sel"], win, st_in.seq_lens, out, lse, pipe.ws)
+    t_cp_plain = timed(plain_path)
+    t_cp_pred = timed(pred_path)
+    print(json.dumps({
+        "probe": "predicted_layers",
+        "workload": f"host, 2 query tokens (speculative = real + N(0, 0.3)), {n_layers} layers with their own inputs",
+        "reps": reps,
+        "plain_us_per_layer": round(t_plain / n_layers, 1),
+        "predicted_us_per_layer": round(t_pred / n_layers, 1),
+        "link_bytes_per_layer_plain": real * chunk // n_layers,
+        "link_bytes_per_layer_predicted": (pref + miss) * chunk // n_layers,
+        "link_bytes_per_layer_after_selection_predicted": miss * chunk // n_layers,
+        "miss_fraction": round(miss / max(1, real), 4),
+        "critical_path_us_plain": round(t_cp_plain, 1),
+        "critical_path_us_predicted": round(t_cp_pred, 1),
+        "note": "per-layer times cover the whole call (prefetches included); the critical path is one "
+                "layer's work after its selection, with the prediction already staged"}), flush=True)
+    return 0
+
+
 def hbm_gather_probe(reps: int, instances: int) -> int:
     """llama32k workload: the stand-alone gather of the selected K/V chunks from
     the HBM pool into staging buffers (in the decode step this gather is fused
@@ -423,6 +507,8 @@ def main() -> int:
                     help="only time the stand-alone gather from the HBM pool (llama32k) and exit")
     ap.add_argument("--cobatched", action="store_true",
                     help="only compare co-batched two-token attention with one launch per token and exit")
+    ap.add_argument("--layers-predicted", action="store_true",
+                    help="only compare the predicted-prefetch layer pipeline with the plain one and exit")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe, max(1, args.steps))
@@ -434,6 +520,8 @@ def main() -> int:
         return hbm_gather_probe(max(1, args.steps), max(1, args.instances))
     if args.hybrid:
         return hybrid_probe(max(1, min(args.steps, 50)))
+    if args.layers_predicted:
+        return predicted_layers_probe(max(1, min(args.steps, 30)))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -523,35 +611,97 @@ def main() -> int:
     step_bytes = statistics.mean(bytes_per_instance)
     tokens_per_s = wl.batch * n_layers / (ms_per_step * 1e-3)
 
-    # ---- dominant kernel: the step itself when it is one launch, else the
-    # attention launch timed alone over the same instances
+    # ---- per-kernel figures.  One launch: the step kernel is the step.  Two
+    # launches (device pool): the attention launch is timed alone over the
+    # same instances, and the scoring launch (scoring with the fused top-k) is
+    # the step minus that (consecutive launches leave no gap between them).
+    # Host pool: the gather (pinned pool -> stage, over the host link) and the
+    # attention of the staged blocks are each timed alone.
     launches = B.sparsekv_decode_step_launches(steps[0].pr)
-    kernel = k_ms = k_bytes = None
-    if launches == 1:
-        kernel, k_ms, k_bytes = "pair_step_kernel", ms_per_step, step_bytes
-    elif wl.pool != "host":
-        sources = []
-        for st in steps:
-            d = st.inp
-            sparse = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
-            sources.append((st, sparse))
+
+    def timed_us(fn) -> float:
         for k in range(args.warmup):
-            st, sp = sources[k % len(sources)]
-            B.sparsekv_attend(st.pr, st.inp.q, sp, st.indices, st.n_sel, sp, st.inp.seq_lens,
-                              st.out, st.lse, st.ws)
+            fn(k)
         torch.cuda.synchronize()
         ev0.record(stream)
         for k in range(args.steps):
-            st, sp = sources[k % len(sources)]
-            B.sparsekv_attend(st.pr, st.inp.q, sp, st.indices, st.n_sel, sp, st.inp.seq_lens,
-                              st.out, st.lse, st.ws)
+            fn(k)
         ev1.record(stream)
         ev1.synchronize()
-        k_ms = ev0.elapsed_time(ev1) / args.steps
-        per_inst = [attention_bytes(wl, s.inp.seq_lens.cpu().numpy(), s.n_sel[:, 0].cpu().numpy())
-                    for s in steps]
-        kernel, k_bytes = "attend_kernel", statistics.mean(per_inst)
-        log(f"attention kernel alone: {k_ms * 1e3:.1f} us, {k_bytes / 1e6:.1f} MB")
+        return ev0.elapsed_time(ev1) * 1e3 / args.steps
+
+    def entry(name, nbytes, us, bound="hbm", note=None):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        e = {"kernel": name, "bytes_per_launch": int(nbytes), "us_per_launch": round(us, 2),
+             "gbps": round(gbps, 1), "bound": bound}
+        if bound == "hbm":
+            e["frac_of_peak"] = round(gbps / HBM_PEAK_GBS, 4)
+        if note:
+            e["note"] = note
+        return e
+
+    # each instance's selection: the decode step's outputs, or for a host
+    # pool those of layer 0 of its pipeline (every layer has the same inputs,
+    # so the staging slots hold this selection's blocks)
+    sels = [(p.outs[0]["indices"], p.outs[0]["n_sel"]) for p in pipes] if pipes else \
+        [(st.indices, st.n_sel) for st in steps]
+
+    def attend_us(staged: bool) -> float:
+        srcs = []
+        for i, st in enumerate(steps):
+            d = st.inp
+            if staged:
+                pipe = pipes[i]
+                sp = B.kv_source(B.SKV_SRC_STAGED, pipe.k_slots[0], pipe.v_slots[0])
+                win = B.kv_source(B.SKV_SRC_WINDOW, d.window_k, d.window_v) if wl.window else None
+            else:
+                sp = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
+                win = sp
+            srcs.append((st, sp, win, sels[i]))
+
+        def one(k):
+            st, sp, win, (idx, nsel) = srcs[k % len(srcs)]
+            B.sparsekv_attend(st.pr, st.inp.q, sp, idx, nsel, win, st.inp.seq_lens, st.out, st.lse, st.ws)
+        return timed_us(one)
+
+    attn_bytes = statistics.mean(attention_bytes(wl, s.inp.seq_lens.cpu().numpy(), sel[1][:, 0].cpu().numpy())
+                                 for s, sel in zip(steps, sels))
+    e_l = configs.ELEM_BYTES[wl.landmark_dtype]
+    score_bytes = statistics.mean(
+        wl.n_kv_heads * sum(configs.n_candidates(int(L), wl.window, wl.block_size) for L in s.inp.seq_lens.cpu())
+        * wl.head_dim * e_l + wl.batch * wl.n_q_tokens * wl.n_q_heads * wl.head_dim * configs.ELEM_BYTES[wl.q_dtype]
+        for s in steps)
+    kernels = []
+    kernel = k_ms = k_bytes = None
+    if launches == 1:
+        kernel, k_ms, k_bytes = "pair_step_kernel", ms_per_step, step_bytes
+        kernels.append(entry(kernel, k_bytes, k_ms * 1e3))
+    elif wl.pool != "host":
+        a_us = attend_us(staged=False)
+        kernel, k_ms, k_bytes = "attend_kernel", a_us * 1e-3, attn_bytes
+        log(f"attention kernel alone: {a_us:.1f} us, {attn_bytes / 1e6:.1f} MB")
+        s_us = ms_per_step * 1e3 - a_us
+        kernels.append(entry("score_kernel", score_bytes, s_us,
+                             note="scoring with the fused top-k; time = step minus the attention launch alone"))
+        kernels.append(entry("attend_kernel", attn_bytes, a_us, note="timed alone over the same instances"))
+    else:
+        a_us = attend_us(staged=True)
+        kernels.append(entry("attend_kernel", attn_bytes, a_us,
+                             note="staged blocks plus the HBM window, timed alone"))
+        link = statistics.mean(configs.host_link_bytes(wl, s.inp.seq_lens.cpu(), s.inp.k_per_seq.cpu())
+                               for s in steps)
+
+        def gather(k):
+            i = k % len(steps)
+            st, pipe, (idx, nsel) = steps[i], pipes[i], sels[i]
+            d = st.inp
+            B.sparsekv_gather(st.pr, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table, idx, nsel,
+                              pipe.k_slots[0], pipe.v_slots[0], pipe.k_slot_scales and pipe.k_slot_scales[0],
+                              pipe.v_slot_scales and pipe.v_slot_scales[0])
+        g_us = timed_us(gather)
+        kernels.append(entry("gather_kernel", link, g_us, bound="host_link",
+                             note="selected K/V read over the host link (and written to the HBM stage), "
+                                  "timed alone"))
 
     roofline = None
     if kernel:
@@ -609,7 +759,9 @@ def main() -> int:
     cfg = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "n_q_heads": wl.n_q_heads,
            "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
            "top_k": wl.top_k, "window": wl.window, "kv_dtype": wl.kv_dtype,
-           "n_q_tokens": wl.n_q_tokens, "pool": wl.pool, "instances": args.instances}
+           "n_q_tokens": wl.n_q_tokens, "pool": wl.pool, "instances": args.instances,
+           "seed": wl.seed, "instance_ids": list(range(args.instances)),
+           "generator": "numpy SeedSequence([seed, instance]).spawn(8) seeding torch cuda generators"}
     if n_layers > 1:
         cfg["layers_per_step"] = n_layers
     line = {
@@ -634,10 +786,12 @@ def main() -> int:
         "step_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "launches_per_step": launches,
         "roofline": roofline,
+        "kernels": kernels,
         "cpu_baseline": cpu,
     }
     if wl.n_q_tokens == 2:
-        line["overlap_mean"] = round(float(steps[0].overlap.mean().item()), 4)
+        ov = pipes[0].outs[0]["overlap"] if pipes else steps[0].overlap
+        line["overlap_mean"] = round(float(ov.mean().item()), 4)
     if wl.pool == "host":
         # the gather's pull over the host link, against a contiguous pinned copy
         link_bytes = n_layers * statistics.mean(configs.host_link_bytes(wl, L, K) for L, K in shapes)
