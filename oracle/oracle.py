@@ -17,10 +17,24 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 DTYPE_CODE = {"fp32": 0, "bf16": 1, "fp8": 2}
+# Host AddressSanitizer + UndefinedBehaviorSanitizer build (clang, LLVM OpenMP),
+# selected with SKV_ORACLE_LIB for a sanitized CPU test run.
+SAN_LIB = os.path.join(_HERE, "_asan", "liboracle.so")
+
+
+def build_sanitized() -> str:
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    subprocess.check_call(["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-fno-omit-frame-pointer", "-fsanitize=address", "-fsanitize=undefined",
+                           "-fno-sanitize-recover=undefined", "-o", SAN_LIB, os.path.join(_HERE, "oracle.c"),
+                           "-lm", "-L/opt/rocm/llvm/lib", "-Wl,-rpath,/opt/rocm/llvm/lib"])
+    return SAN_LIB
 
 
 def build(force: bool = False) -> str:
     """Compile oracle.c into liboracle.so with gcc (OpenMP over (b, g))."""
+    if os.environ.get("SKV_ORACLE_LIB"):
+        return os.environ["SKV_ORACLE_LIB"]
     src = os.path.join(_HERE, "oracle.c")
     if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < max(
             os.path.getmtime(src), os.path.getmtime(os.path.join(_HERE, "oracle.h"))):
@@ -45,8 +59,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = C.CDLL(LIB_PATH)
+        L = C.CDLL(build())
         L.orc_bf16_value.restype = C.c_double
         L.orc_bf16_value.argtypes = [C.c_uint16]
         L.orc_e4m3fn_value.restype = C.c_double

@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsparsekv.so")
+# SKV_LIB selects another build of the library (the host-sanitized one under _asan/)
+LIB_PATH = os.environ.get("SKV_LIB") or os.path.join(_HERE, "libsparsekv.so")
 
 SKV_OK, SKV_E_NULL, SKV_E_SHAPE, SKV_E_DTYPE, SKV_E_UNSUPPORTED, SKV_E_WORKSPACE, SKV_E_HIP = range(7)
 SKV_F32, SKV_BF16, SKV_FP8_E4M3FN = range(3)

@@ -23,23 +23,37 @@ CXX = os.environ.get("CXX_HOST", "g++")
 # x86-64-v3 (AVX2, FMA, F16C): every MI355X host CPU has it
 CXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fopenmp", "-march=x86-64-v3", "-Wall"]
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (CPU runs only:
+# the device code is not instrumented).  Everything is compiled with clang so
+# that one sanitizer runtime (clang's, preloaded) serves the whole process.
+SAN_DIR = os.path.join(HERE, "_asan")
+SAN_LIB = os.path.join(SAN_DIR, "libsparsekv.so")
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+SAN = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined"]
+SAN_HIP = [f for flag in SAN for f in ("-Xarch_host", flag)] + ["-Xarch_host", "-fno-omit-frame-pointer",
+                                                                "-Xarch_host", "-g"]
+SAN_CXX = ["-O1", "-g", "-std=c++17", "-fPIC", "-fopenmp", "-march=x86-64-v3", "-fno-omit-frame-pointer", *SAN]
+
 
 def sources(src_dir: str = CSRC) -> list[str]:
     return sorted(glob.glob(os.path.join(src_dir, "*.hip")) + glob.glob(os.path.join(src_dir, "*.cpp")))
 
 
 def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD_DIR,
-          src_dir: str = CSRC) -> str:
-    """Compile every HIP source and link the shared library; always rebuilds."""
+          src_dir: str = CSRC, sanitize: bool = False) -> str:
+    """Compile every HIP source and link the shared library; always rebuilds.
+    sanitize=True builds the host-sanitized library into _asan/ instead."""
+    if sanitize:
+        out, build_dir = SAN_LIB, os.path.join(SAN_DIR, "obj")
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources(src_dir)
 
     def compile_one(src: str) -> str:
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         if src.endswith(".cpp"):
-            cmd = [CXX, *CXX_FLAGS, "-c", src, "-o", obj]
+            cmd = [CLANGXX, *SAN_CXX, "-c", src, "-o", obj] if sanitize else [CXX, *CXX_FLAGS, "-c", src, "-o", obj]
         else:
-            cmd = [HIPCC, *FLAGS, *extra_flags, "-c", src, "-o", obj]
+            cmd = [HIPCC, *FLAGS, *(SAN_HIP if sanitize else ()), *extra_flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"{cmd[0]} failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -51,7 +65,12 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str 
         objs = list(ex.map(compile_one, srcs))
     tmp = out + ".tmp"
     # the host code's OpenMP runtime is GCC's (the one the rest of the process uses)
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lgomp"]
+    if sanitize:
+        # the sanitizer runtime and LLVM's OpenMP runtime come from the preloaded process
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+               "-L/opt/rocm/llvm/lib", "-lomp", "-Wl,-rpath,/opt/rocm/llvm/lib"]
+    else:
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, "-lgomp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
@@ -60,4 +79,5 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str 
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))
