@@ -198,6 +198,17 @@ def test_two_level_selection_ties_go_to_lowest_ids():
     assert np.all(gi == np.arange(16)[None, None, None, :])
 
 
+# More two-level shapes: one token over 32 chunks of 256 rows; two tokens over
+# 4 chunks of 1024 rows; k = 100 (not a power of two) over 8 chunks of 512.
+@pytest.mark.parametrize("wl", [
+    configs.LLAMA32K.scaled(batch=1, context=262144),
+    configs.DUAL.scaled(batch=8),
+    configs.DUAL.scaled(top_k=100),
+], ids=["one_token_32_chunks", "two_tokens_1024_rows", "k_100"])
+def test_two_level_selection_shapes(wl):
+    check_step(wl, gen_device="cuda")
+
+
 # ------------------------------------------------ single-launch step (>= 128 pairs)
 # 16 sequences x 8 KV heads: decode_step runs as one launch, one workgroup per pair
 MIXED16 = [4096, 1000, 513, 37, 0, 1, 512, 513, 4000, 2048, 3333, 4095, 64, 700, 2500, 4096]
