@@ -271,8 +271,9 @@ def predicted_layers_probe(reps: int, n_layers: int = 4) -> int:
     pk, pv = pipe.k_slots[0], pipe.v_slots[0]
     k_st, v_st = pipe.stage[0], pipe.stage[1]
     B.sparsekv_gather(pipe.pr, *pools, preds[0][0][:, 1:], preds[0][1][:, 1:], pk, pv, None, None)
-    sp = B.kv_source(B.SKV_SRC_STAGED, k_st, v_st)
-    win = B.kv_source(B.SKV_SRC_WINDOW, st_in.window_k, st_in.window_v)
+    sp = B.kv_source(B.SKV_SRC_STAGED, k_st, v_st, pipe.stage[2], pipe.stage[3])
+    win = B.kv_source(B.SKV_SRC_WINDOW, st_in.window_k, st_in.window_v, st_in.window_k_scales,
+                      st_in.window_v_scales)
     out = torch.empty_like(o0["out"])
     lse = torch.empty_like(o0["lse"])
 
@@ -652,8 +653,11 @@ def main() -> int:
             d = st.inp
             if staged:
                 pipe = pipes[i]
-                sp = B.kv_source(B.SKV_SRC_STAGED, pipe.k_slots[0], pipe.v_slots[0])
-                win = B.kv_source(B.SKV_SRC_WINDOW, d.window_k, d.window_v) if wl.window else None
+                sp = B.kv_source(B.SKV_SRC_STAGED, pipe.k_slots[0], pipe.v_slots[0],
+                                 pipe.k_slot_scales[0] if pipe.k_slot_scales else None,
+                                 pipe.v_slot_scales[0] if pipe.v_slot_scales else None)
+                win = B.kv_source(B.SKV_SRC_WINDOW, d.window_k, d.window_v, d.window_k_scales,
+                                  d.window_v_scales) if wl.window else None
             else:
                 sp = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
                 win = sp

@@ -37,7 +37,9 @@
  *   indices    [B][T][Hkv][k_max] int32, ascending block ids, -1 padded
  *   n_sel      [B][T][Hkv] int32 = min(k_b, #candidates)
  *   stage      [B][Hkv][k_max][blk][d] kv_dtype; stage scales [B][Hkv][k_max]
- *   window buf [B][Hkv][W][d] kv_dtype: row r holds position ws_b + r
+ *   window buf [B][Hkv][W][d] kv_dtype: row r holds position ws_b + r;
+ *              fp8: per-row scales [B][Hkv][W] fp32 (row r's K and V scales,
+ *              normally those of the pool block holding position ws_b + r)
  *   out        [B][Hq][d] fp32 (real token), lse [B][Hq] fp32 (natural log);
  *              co-batched attention: [B][T][Hq][d] and [B][T][Hq]
  *   overlap    [B][Hkv] fp32 = |I_real & I_spec| / |I_real| (T == 2)
@@ -116,13 +118,15 @@ typedef struct {
 typedef enum {
     SKV_SRC_PAGED = 0,   /* pool chunks through block_table (and indices for the sparse part) */
     SKV_SRC_STAGED = 1,  /* gathered stage buffers, slot m = m-th selected block */
-    SKV_SRC_WINDOW = 2   /* window buffers [B][Hkv][W][d]; needs W % blk == 0; not fp8 */
+    SKV_SRC_WINDOW = 2   /* window buffers [B][Hkv][W][d]; needs W % blk == 0 */
 } skv_source_kind;
 
 typedef struct {
     int32_t kind;                /* skv_source_kind */
     const void *k, *v;           /* pool, stage or window buffers */
-    const float *k_scales, *v_scales;  /* fp8: pool [P][Hkv] or stage [B][Hkv][k_max] */
+    const float *k_scales, *v_scales;  /* fp8: pool [P][Hkv], stage [B][Hkv][k_max] or
+                                          window buffer [B][Hkv][W] (one per row,
+                                          16-byte aligned) */
     const int32_t *block_table;  /* PAGED only */
 } skv_kv_source;
 
@@ -133,6 +137,10 @@ typedef struct {
     const float *k_scales, *v_scales;  /* fp8 only */
     const int32_t *block_table, *seq_lens, *k_per_seq;
     const void *window_k, *window_v;   /* host pools: HBM window buffers; else NULL */
+    /* fp8 host pools with W > 0: the window buffers' per-row scales
+       [B][Hkv][W] fp32 (16-byte aligned); else NULL.  fp8 device pools
+       take no window buffers (SKV_E_UNSUPPORTED). */
+    const float *window_k_scales, *window_v_scales;
 } skv_step_inputs;
 
 /* Per-layer outputs of a full decode step. */
@@ -272,7 +280,7 @@ skv_status sparsekv_gather_correct(const skv_problem *pr, const void *k_pool, co
  *   log-sum-exp into out (fp32) and lse = ln sum_p e^{z_p}.
  * Empty parts contribute nothing; with no position at all, out = 0 and
  * lse = -inf.  sparse->kind is PAGED (indices index the block table) or
- * STAGED; window->kind is PAGED or WINDOW.
+ * STAGED; window->kind is PAGED or WINDOW (fp8: with per-row scales).
  */
 skv_status sparsekv_attend(const skv_problem *pr, const void *q, const skv_kv_source *sparse,
                            const int32_t *indices, const int32_t *n_sel,
@@ -290,8 +298,8 @@ skv_status sparsekv_attend(const skv_problem *pr, const void *q, const skv_kv_so
  * two selections is read once per (sequence, KV head); a block that only one
  * token selected is masked for the other.  out is [B][T][Hq][d] fp32, lse
  * [B][T][Hq] (may be NULL).  T == 2 needs a device pool and a PAGED sparse
- * source (the union is read through the block table); SKV_E_UNSUPPORTED
- * otherwise.  T == 1 is sparsekv_attend.  The workspace is the
+ * source (the union is read through the block table), and fp8 a PAGED
+ * window source; SKV_E_UNSUPPORTED otherwise.  T == 1 is sparsekv_attend.  The workspace is the
  * one sparsekv_workspace_size gives for the problem.
  */
 skv_status sparsekv_attend_cobatched(const skv_problem *pr, const void *q,
@@ -380,8 +388,8 @@ skv_status sparsekv_host_attention(const skv_problem *pr, const skv_host_part *h
  * The results equal sparsekv_decode_step's up to fp32 rounding.  The call
  * blocks the calling thread until the selection has reached the host and
  * the sparse part is done (the window attention runs meanwhile); the fusion
- * is enqueued on `stream` and runs asynchronously.  fp8 pools need window
- * 0 (fp8 window buffers are not supported).
+ * is enqueued on `stream` and runs asynchronously.  fp8 window buffers
+ * take their per-row scales from in->window_k_scales / window_v_scales.
  */
 skv_status sparsekv_decode_step_hybrid(const skv_problem *pr, const skv_step_inputs *in,
                                        const skv_step_outputs *out, const skv_host_part *host,

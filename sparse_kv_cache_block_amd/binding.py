@@ -56,7 +56,8 @@ class StepInputs(C.Structure):
     _fields_ = [("q", C.c_void_p), ("landmarks", C.c_void_p), ("k_pool", C.c_void_p),
                 ("v_pool", C.c_void_p), ("k_scales", C.c_void_p), ("v_scales", C.c_void_p),
                 ("block_table", C.c_void_p), ("seq_lens", C.c_void_p), ("k_per_seq", C.c_void_p),
-                ("window_k", C.c_void_p), ("window_v", C.c_void_p)]
+                ("window_k", C.c_void_p), ("window_v", C.c_void_p),
+                ("window_k_scales", C.c_void_p), ("window_v_scales", C.c_void_p)]
 
 
 class StepOutputs(C.Structure):
@@ -243,9 +244,10 @@ def sparsekv_attend_cobatched(pr: Problem, q, sparse: KvSource, indices, n_sel, 
 
 
 def step_inputs(q, landmarks, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, k_per_seq,
-                window_k=None, window_v=None) -> StepInputs:
+                window_k=None, window_v=None, window_k_scales=None, window_v_scales=None) -> StepInputs:
     return StepInputs(*(_ptr(x) for x in (q, landmarks, k_pool, v_pool, k_scales, v_scales,
-                                          block_table, seq_lens, k_per_seq, window_k, window_v)))
+                                          block_table, seq_lens, k_per_seq, window_k, window_v,
+                                          window_k_scales, window_v_scales)))
 
 
 def step_outputs(indices, n_sel, out, lse=None, overlap=None) -> StepOutputs:

@@ -12,7 +12,8 @@ namespace skv {
 constexpr int kAttnWaves = 8;                 // waves per attention workgroup
 constexpr int kAttnThreads = kAttnWaves * kWave;
 
-template <int KV, int D, int BLK>
+// WROW: fp8 window buffers with one scale per row (host pools).
+template <int KV, int D, int BLK, bool WROW = false>
 __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   using C = AttnCfg<KV, D, BLK>;
   __shared__ __attribute__((aligned(16))) char smem[attn_lds_bytes<KV, D, BLK>(kAttnWaves)];
@@ -26,7 +27,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnParams p) {
   const int ips = (total + p.n_splits - 1) / p.n_splits;
   const int first = split * ips;
   const int count = max(0, min(ips, total - first));
-  attend_items<KV, D, BLK, kAttnWaves>(
+  attend_items<KV, D, BLK, kAttnWaves, 1, true, kLateStrided, WROW>(
       p, smem, b, g, first, count, count, 0,
       [&](int item) { return describe<KV, D, BLK>(p, b, g, item, nsel, ws); },
       [](int) { return ItemDesc{0, 0, 0}; }, [] {}, [](auto&& issue_first) { issue_first(); }, [] {});
@@ -157,10 +158,13 @@ __global__ __launch_bounds__(kAttnThreads) void attend_cobatched_kernel(AttnPara
 
 template <int KV, int D>
 static hipError_t launch_blk(const AttnParams& p, dim3 grid, hipStream_t s, bool cob) {
+  // fp8 window buffers carry one scale per row
+  const bool wrow = KV == KV_FP8 && p.window > 0 && p.window_kind == SKV_SRC_WINDOW;
   switch (p.blk) {
 #define SKV_ATTEND_CASE(BLK)                                                                          \
   case BLK:                                                                                           \
     if (cob) hipLaunchKernelGGL((attend_cobatched_kernel<KV, D, BLK>), grid, dim3(kAttnThreads), 0, s, p); \
+    else if (wrow) hipLaunchKernelGGL((attend_kernel<KV, D, BLK, KV == KV_FP8>), grid, dim3(kAttnThreads), 0, s, p); \
     else hipLaunchKernelGGL((attend_kernel<KV, D, BLK>), grid, dim3(kAttnThreads), 0, s, p);           \
     break;
     SKV_ATTEND_CASE(16)

@@ -162,12 +162,15 @@ __device__ __forceinline__ int window_blocks(const AttnParams& p, int L, int ws)
 // PAD_FIRST a wave without one issues the same loads from row 0 of its
 // source, so every path has the same count of loads in flight; without it
 // such a wave issues nothing and reaches post() at once.  post() runs after
-// pre (both hooks run in every thread).  Leaves each wave's unnormalised O rows, running max
-// and sum in its LDS combine region.
+// pre (both hooks run in every thread).  WROW (fp8 only): the window source
+// is a window buffer whose every row has its own K and V scale (p.wks / p.wvs
+// [B][Hkv][W], row r of the pair at (b * Hkv + g) * W + r); each token's
+// logit and probability then take its row's scales.  Leaves each wave's
+// unnormalised O rows, running max and sum in its LDS combine region.
 constexpr int kLateStrided = 0, kLateShared = 1;
 
 template <int KV, int D, int BLK, int NW, int NTOK = 1, bool PAD_FIRST = true, int LATE = kLateStrided,
-          class EarlyDescFn, class LateDescFn, class LateReadyFn, class PreFn, class PostFn>
+          bool WROW = false, class EarlyDescFn, class LateDescFn, class LateReadyFn, class PreFn, class PostFn>
 __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, int b, int g, int first,
                                              int count, int n_early, int early_wave0, EarlyDescFn desc_early,
                                              LateDescFn desc_late, LateReadyFn late_ready, PreFn pre,
@@ -244,6 +247,12 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
   uint4 vr[C::NV];
   int pos0 = 0, skip = 0;
   float ksc = 1.f, vsc = 1.f;
+  // WROW: the K and V scales of the tokens this lane's logits belong to
+  // (token 16 * tile + 4 * kg + r of the slice is element r of tile)
+  constexpr int NWS = WROW ? C::NT : 1;
+  f32x4_t ksw[NWS], vsw[NWS];
+#pragma unroll
+  for (int t = 0; t < NWS; ++t) ksw[t] = vsw[t] = f32x4_t{1.f, 1.f, 1.f, 1.f};
 
   // Issue the loads of the slice `sub` of `row` (pos0 already set).
   auto issue = [&](int row, int sub) {
@@ -258,11 +267,18 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
     else off = (int64_t)row * D;
     off += (int64_t)sub * C::TB * D;
     if constexpr (KV == KV_FP8) {
-      // paged: per (block, head) scales; staged: per slot (fp8 window buffers are rejected)
+      // paged: per (block, head) scales; staged: per slot; window buffer: per row (WROW)
       if (kind != SKV_SRC_WINDOW) {
         const int64_t si = kind == SKV_SRC_PAGED ? (int64_t)row * p.Hkv + g : row;
         ksc = (win ? p.wks : p.sks)[si];
         vsc = (win ? p.wvs : p.svs)[si];
+      } else if constexpr (WROW) {
+        const int64_t r0 = (int64_t)row + sub * C::TB;   // the slice's first row of the window buffer
+#pragma unroll
+        for (int tile = 0; tile < NWS; ++tile) {
+          ksw[tile] = *reinterpret_cast<const f32x4_t*>(p.wks + r0 + 16 * tile + 4 * kg);
+          vsw[tile] = *reinterpret_cast<const f32x4_t*>(p.wvs + r0 + 16 * tile + 4 * kg);
+        }
       }
     }
     const char* kb = (win ? kbase_w : kbase_s) + off * C::ES;
@@ -327,6 +343,14 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
     const int lo = win ? ws : 0;
     const int hi = win ? L : ws;
     const float ks_cur = ksc, vs_cur = vsc;
+    // per-row scales of a window-buffer slice (WROW), else the item's scales
+    const bool rows_scaled = WROW && win;
+    f32x4_t ksw_cur[NWS], vsw_cur[NWS];
+#pragma unroll
+    for (int t = 0; t < NWS; ++t) {
+      ksw_cur[t] = ksw[t];
+      vsw_cur[t] = vsw[t];
+    }
     // a co-batched item that one token did not select is masked in that token's columns
     const bool col_ok = NTOK == 1 || !((skip >> tq) & 1);
 
@@ -396,8 +420,11 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pos = p0 + 16 * tile + 4 * kg + r;
-        float z = st[tile][r] * sc;
-        z = (pos >= lo && pos < hi && col_ok) ? z : -INFINITY;
+        const bool in_range = pos >= lo && pos < hi && col_ok;
+        float z = st[tile][r] * (rows_scaled ? p.qk_scale * ksw_cur[tile < NWS ? tile : 0][r] : sc);
+        z = in_range ? z : -INFINITY;
+        // a window-buffer row outside the window may hold any scale
+        if constexpr (WROW) vsw_cur[tile < NWS ? tile : 0][r] = in_range ? vsw_cur[tile < NWS ? tile : 0][r] : 0.f;
         st[tile][r] = z;
         bm = fmaxf(bm, z);
       }
@@ -456,7 +483,15 @@ __device__ __forceinline__ void attend_items(const AttnParams& p, char* smem, in
           const int t0 = 2 * hh + (2 * e2) / 4;
           const int tc = t0 < NT ? t0 : NT - 1;
           f32x2_t pv = {t0 < NT ? st[tc][(2 * e2) % 4] : 0.f, t0 < NT ? st[tc][(2 * e2 + 1) % 4] : 0.f};
-          if constexpr (KV == KV_FP8) pv *= vs_cur;
+          if constexpr (KV == KV_FP8) {
+            if (rows_scaled) {
+              const int tw = tc < NWS ? tc : 0;
+              pv.x *= vsw_cur[tw][(2 * e2) % 4];
+              pv.y *= vsw_cur[tw][(2 * e2 + 1) % 4];
+            } else {
+              pv *= vs_cur;
+            }
+          }
           const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf16x2_t));
           const f32x2_t rest = {pv.x - bf16_lo(hw), pv.y - bf16_hi(hw)};
           const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, bf16x2_t));

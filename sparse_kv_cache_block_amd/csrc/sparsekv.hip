@@ -244,9 +244,11 @@ skv_status set_source(const skv_problem& p, AttnParams& a, const skv_kv_source* 
   if (!src->k || !src->v) return fail(SKV_E_NULL, "%s source K/V is NULL", sparse ? "sparse" : "window");
   SKV_TRY(check_align16(sparse ? "sparse source" : "window source", {src->k, src->v}));
   const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
-  if (!sparse && src->kind == SKV_SRC_WINDOW && fp8) return fail(SKV_E_UNSUPPORTED, "fp8 window buffers");
   if (fp8 && (!src->k_scales || !src->v_scales))
     return fail(SKV_E_NULL, "fp8 %s source needs scales", sparse ? "sparse" : "window");
+  // fp8 window buffers: one scale per row, read four rows at a time
+  if (fp8 && !sparse && src->kind == SKV_SRC_WINDOW)
+    SKV_TRY(check_align16("window scales", {src->k_scales, src->v_scales}));
   if (sparse) {
     if (src->kind != SKV_SRC_PAGED && src->kind != SKV_SRC_STAGED)
       return fail(SKV_E_UNSUPPORTED, "sparse source kind %d", src->kind);
@@ -325,8 +327,15 @@ skv_status check_step_io(const skv_problem& p, const skv_step_inputs* in, const 
     return fail(SKV_E_NULL, "host pools need HBM window buffers");
   if (p.kv_dtype == SKV_FP8_E4M3FN && (!in->k_scales || !in->v_scales))
     return fail(SKV_E_NULL, "fp8 pools need scales");
+  if (p.kv_dtype == SKV_FP8_E4M3FN && p.window > 0 && in->window_k) {
+    // the device pool's fused step reads the window from the pool itself
+    if (p.pool_location == SKV_POOL_DEVICE)
+      return fail(SKV_E_UNSUPPORTED, "fp8 window buffers serve host pools only");
+    if (!in->window_k_scales || !in->window_v_scales)
+      return fail(SKV_E_NULL, "fp8 window buffers need per-row scales");
+  }
   SKV_TRY(check_align16("decode step", {in->q, in->landmarks, in->k_pool, in->v_pool, in->window_k,
-                                        in->window_v}));
+                                        in->window_v, in->window_k_scales, in->window_v_scales}));
   return SKV_OK;
 }
 
@@ -460,7 +469,7 @@ skv_status prepare_host_layer(const skv_problem& p, const Plan& pl, const skv_st
   skv_kv_source sparse{SKV_SRC_STAGED, k_stage, v_stage, k_stage_scales, v_stage_scales, nullptr};
   SKV_TRY(set_source(p, hl->a, &sparse, true));
   if (p.window > 0) {
-    skv_kv_source win{SKV_SRC_WINDOW, in.window_k, in.window_v, nullptr, nullptr, nullptr};
+    skv_kv_source win{SKV_SRC_WINDOW, in.window_k, in.window_v, in.window_k_scales, in.window_v_scales, nullptr};
     SKV_TRY(set_source(p, hl->a, &win, false));
   } else {
     hl->a.window_kind = SKV_SRC_WINDOW;  // no window splits are launched
@@ -734,6 +743,8 @@ skv_status sparsekv_attend_cobatched(const skv_problem* pr, const void* q, const
     return fail(SKV_E_UNSUPPORTED, "attend_cobatched reads the union of the selections from a paged source");
   if (p.pool_location != SKV_POOL_DEVICE)
     return fail(SKV_E_UNSUPPORTED, "attend_cobatched needs a device pool");
+  if (p.kv_dtype == SKV_FP8_E4M3FN && p.window > 0 && window && window->kind == SKV_SRC_WINDOW)
+    return fail(SKV_E_UNSUPPORTED, "attend_cobatched: fp8 window buffers");
   const Plan pl = make_plan(p);
   SKV_TRY(check_ws(pl, workspace, workspace_bytes));
   char* ws = static_cast<char*>(workspace);
@@ -829,7 +840,6 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
   SKV_TRY(check_step_io(p, in, out));
   SKV_TRY(check_host_part(p, host));
   const bool fp8 = p.kv_dtype == SKV_FP8_E4M3FN;
-  if (fp8 && p.window > 0) return fail(SKV_E_UNSUPPORTED, "hybrid step: fp8 window buffers");
   if (p.window > 0 && p.window % p.block_size != 0)
     return fail(SKV_E_SHAPE, "hybrid step: window buffers need window %% block_size == 0");
   const Plan pl = make_plan(p);
@@ -846,10 +856,13 @@ skv_status sparsekv_decode_step_hybrid(const skv_problem* pr, const skv_step_inp
   AttnParams a{};
   if (p.window > 0) {
     a = attn_params(p, pl, in->q, in->seq_lens, o_win, lse_win, ws);
-    skv_kv_source win{SKV_SRC_WINDOW, in->window_k, in->window_v, nullptr, nullptr, nullptr};
+    skv_kv_source win{SKV_SRC_WINDOW, in->window_k, in->window_v, in->window_k_scales, in->window_v_scales,
+                      nullptr};
     SKV_TRY(set_source(p, a, &win, false));
-    // no sparse item is attended; waves without an item read row 0 of the window buffers
-    skv_kv_source none{SKV_SRC_STAGED, in->window_k, in->window_v, nullptr, nullptr, nullptr};
+    // no sparse item is attended; waves without an item read row 0 of the
+    // window buffers (and, fp8, the first of their scales)
+    skv_kv_source none{SKV_SRC_STAGED, in->window_k, in->window_v, in->window_k_scales, in->window_v_scales,
+                       nullptr};
     SKV_TRY(set_source(p, a, &none, true));
     a.indices = out->indices;
     a.n_sel = out->n_sel;

@@ -66,6 +66,8 @@ class DecodeInputs:
     pool_layout: str           # "block_major" [P][Hkv][blk][d] or "head_major" [Hkv][P][blk][d]
     window_k: Optional[torch.Tensor] = None   # [B][Hkv][W][d] (host pool only)
     window_v: Optional[torch.Tensor] = None
+    window_k_scales: Optional[torch.Tensor] = None   # [B][Hkv][W] fp32 (host pool, fp8 only)
+    window_v_scales: Optional[torch.Tensor] = None
     extras: dict = field(default_factory=dict)
 
     @property
@@ -95,6 +97,7 @@ class DecodeInputs:
             block_table=mv(self.block_table), seq_lens=mv(self.seq_lens),
             k_per_seq=mv(self.k_per_seq), n_pool_blocks=self.n_pool_blocks,
             pool_layout=self.pool_layout, window_k=mv(self.window_k), window_v=mv(self.window_v),
+            window_k_scales=mv(self.window_k_scales), window_v_scales=mv(self.window_v_scales),
             extras=dict(self.extras))
 
 
@@ -252,21 +255,37 @@ def make_inputs(wl: Workload, device="cpu", instance: int = 0,
                 _fill_code(codes, idx, nan_code)
 
     # ---- recent-window buffers for the host-resident pool ----------------
-    window_k = window_v = None
+    # Row r of pair (b, g) holds position ws_b + r; fp8 rows keep their pool
+    # block's scales, one per row.  Rows past the window's end are unused:
+    # zero, or with poison on, NaN codes and NaN scales.
+    window_k = window_v = window_ks = window_vs = None
     if head_major:
         W = wl.window
         window_k = torch.zeros((B, Hkv, W, d), dtype=k_codes.dtype, device=device)
         window_v = torch.zeros((B, Hkv, W, d), dtype=v_codes.dtype, device=device)
+        if k_scales is not None:
+            window_ks = torch.ones((B, Hkv, W), dtype=torch.float32, device=device)
+            window_vs = torch.ones((B, Hkv, W), dtype=torch.float32, device=device)
         for b in range(B):
             L = lens_list[b]
             ws = max(0, L - W)
             pos = torch.arange(ws, L, device=device)
-            if pos.numel() == 0:
+            n = pos.numel()
+            if wl.poison and n < W:
+                for codes in (window_k, window_v):
+                    _fill_code(codes, (b, slice(None), slice(n, None)), _nan_code(wl.kv_dtype))
+                if window_ks is not None:
+                    window_ks[b, :, n:] = float("nan")
+                    window_vs[b, :, n:] = float("nan")
+            if n == 0:
                 continue
             phys = block_table[b].to(device)[pos // blk]
             rows = pos % blk
-            window_k[b, :, :pos.numel()] = k_codes[:, phys, rows].reshape(Hkv, -1, d)
-            window_v[b, :, :pos.numel()] = v_codes[:, phys, rows].reshape(Hkv, -1, d)
+            window_k[b, :, :n] = k_codes[:, phys, rows].reshape(Hkv, -1, d)
+            window_v[b, :, :n] = v_codes[:, phys, rows].reshape(Hkv, -1, d)
+            if window_ks is not None:
+                window_ks[b, :, :n] = k_scales[phys].transpose(0, 1)
+                window_vs[b, :, :n] = v_scales[phys].transpose(0, 1)
 
     extras = {}
     if salient is not None:
@@ -278,7 +297,8 @@ def make_inputs(wl: Workload, device="cpu", instance: int = 0,
         seq_lens=torch.tensor(lens_list, dtype=torch.int32, device=device),
         k_per_seq=torch.tensor(ks, dtype=torch.int32, device=device),
         n_pool_blocks=P, pool_layout="head_major" if head_major else "block_major",
-        window_k=window_k, window_v=window_v, extras=extras)
+        window_k=window_k, window_v=window_v, window_k_scales=window_ks, window_v_scales=window_vs,
+        extras=extras)
 
 
 def _nan_code(dtype: str) -> int:

@@ -55,7 +55,8 @@ class DecodeStep:
                                        for _ in range(2)]
         self.inputs = B.step_inputs(inp.q, inp.landmarks, inp.k_pool, inp.v_pool, inp.k_scales,
                                     inp.v_scales, inp.block_table, inp.seq_lens, inp.k_per_seq,
-                                    inp.window_k, inp.window_v)
+                                    inp.window_k, inp.window_v,
+                                    inp.window_k_scales, inp.window_v_scales)
         self.outputs = B.step_outputs(self.indices, self.n_sel, self.out, self.lse, self.overlap)
 
     def run(self, stream=None, copy_stream=None, slot: int = 0) -> None:
@@ -115,7 +116,8 @@ class LayerPipeline:
             o["struct"] = B.step_outputs(o["indices"], o["n_sel"], o["out"], o["lse"], o["overlap"])
             self.outs.append(o)
         self.inputs = [B.step_inputs(inp.q, inp.landmarks, inp.k_pool, inp.v_pool, inp.k_scales, inp.v_scales,
-                                     inp.block_table, inp.seq_lens, inp.k_per_seq, inp.window_k, inp.window_v)
+                                     inp.block_table, inp.seq_lens, inp.k_per_seq, inp.window_k, inp.window_v,
+                                    inp.window_k_scales, inp.window_v_scales)
                        for inp in layers]
         self.k_slots, self.v_slots, self.k_slot_scales, self.v_slot_scales = _stage_slots(layers[0], km, 2, device)
         self.stage = None

@@ -204,9 +204,14 @@ def test_hybrid_step_validation(lib):
     fp8 = B.make_problem(2, 1, 8, 2, 128, 32, 64, 128, 2 * 32 * 128, 32 * 128, 64, 8, "bf16", "fp8", "bf16",
                          pool_location=B.SKV_POOL_HOST)
     host8 = B.HostPart(d, d, 0, d, d, d, d, d, d, d, d, d)
+    # fp8 window buffers need their per-row scales, 16-byte aligned
     assert lib.sparsekv_decode_step_hybrid(C.byref(fp8), C.byref(ins), C.byref(outs), C.byref(host8), d,
-                                           B.sparsekv_workspace_size(fp8), None) == B.SKV_E_UNSUPPORTED
-    assert "fp8 window" in B.sparsekv_last_error()
+                                           B.sparsekv_workspace_size(fp8), None) == B.SKV_E_NULL
+    assert "per-row scales" in B.sparsekv_last_error()
+    ins8 = B.StepInputs(d, d, d, d, d, d, d, d, d, d, d, d, d + 4)
+    assert lib.sparsekv_decode_step_hybrid(C.byref(fp8), C.byref(ins8), C.byref(outs), C.byref(host8), d,
+                                           B.sparsekv_workspace_size(fp8), None) == B.SKV_E_SHAPE
+    assert "aligned" in B.sparsekv_last_error()
     assert lib.sparsekv_decode_step_hybrid(C.byref(hp), C.byref(ins), C.byref(outs), C.byref(host), d, 16,
                                            None) == B.SKV_E_WORKSPACE
 
@@ -304,16 +309,18 @@ def _host_problem(**kw):
                           "bf16", base["kv_dtype"], "bf16", pool_location=B.SKV_POOL_HOST)
 
 
-@pytest.mark.parametrize("kw,status,text", [
-    (dict(kv_dtype="fp8"), B.SKV_E_UNSUPPORTED, "fp8 window"),
-    (dict(window=48), B.SKV_E_SHAPE, "window"),
+@pytest.mark.parametrize("kw,scales,status,text", [
+    (dict(kv_dtype="fp8"), (None, None), B.SKV_E_NULL, "per-row scales"),
+    (dict(kv_dtype="fp8"), (D, None), B.SKV_E_NULL, "per-row scales"),
+    (dict(kv_dtype="fp8"), (D, D + 8), B.SKV_E_SHAPE, "aligned"),
+    (dict(window=48), (None, None), B.SKV_E_SHAPE, "window"),
 ])
-def test_host_pool_window_checked_before_any_launch(lib, kw, status, text):
+def test_host_pool_window_checked_before_any_launch(lib, kw, scales, status, text):
     # the window-source checks run before the scoring launch (dummy pointers:
     # a launch would fail here with SKV_E_HIP, not with these statuses)
     pr = _host_problem(**kw)
     n = B.sparsekv_workspace_size(pr)
-    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D)
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D, *scales)
     outs = B.StepOutputs(D, D, D, D, None)
     assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), D, D, D, D, D, n, None,
                                     None) == status
@@ -326,6 +333,18 @@ def test_host_pool_window_checked_before_any_launch(lib, kw, status, text):
     preds = (B.LayerPrediction * 3)(*[B.LayerPrediction(D, D, 0, None)] * 3)
     assert lib.sparsekv_decode_layers_predicted(C.byref(pr), 3, ins3, outs3, preds, slots, slots, slots, slots,
                                                 0x10000000, 0x20000000, D, D, D, n, None, None) == status
+
+
+def test_fp8_window_buffers_rejected_for_device_pools(lib):
+    # the device pool's fused step reads the window from the pool itself
+    pr = _good_problem(kv_dtype="fp8")
+    n = B.sparsekv_workspace_size(pr)
+    ins = B.StepInputs(D, D, D, D, D, D, D, D, D, D, D, D, D)
+    outs = B.StepOutputs(D, D, D, D, None)
+    assert lib.sparsekv_decode_step(C.byref(pr), C.byref(ins), C.byref(outs), None, None, None, None, D, n,
+                                    None, None) == B.SKV_E_UNSUPPORTED
+    assert "host pools only" in B.sparsekv_last_error()
+    assert lib.sparsekv_decode_step_noalloc(C.byref(pr), C.byref(ins), C.byref(outs), None) == B.SKV_E_UNSUPPORTED
 
 
 def test_host_pool_staging_checked_before_any_launch(lib):

@@ -106,6 +106,21 @@ def test_host_pool_small():
     check_step(configs.HOST.scaled(batch=2, context=8192))
 
 
+# fp8 window buffers of a host pool: each row carries the K and V scales of
+# the pool block its position lives in.  With poison on, the rows past each
+# window's end hold NaN codes and NaN scales, and free blocks NaN codes.
+FP8_WIN = configs.HOST.scaled(batch=3, context=8192, kv_dtype="fp8", poison=True)
+
+
+@pytest.mark.parametrize("wl,lens", [
+    (FP8_WIN, [8192, 300, 0]),                # a window shorter than W, an empty sequence
+    (FP8_WIN.scaled(block_size=16, window=256, head_dim=64), [8192, 5000, 200]),
+    (FP8_WIN.scaled(block_size=32, n_q_tokens=2, spec_noise=0.3), [8192, 4100, 1500]),
+])
+def test_host_pool_fp8_window(wl, lens):
+    check_step(wl, seq_lens=lens)
+
+
 @pytest.mark.parametrize("kw", [
     dict(window=0),
     dict(top_k=90),
@@ -577,6 +592,8 @@ def check_hybrid(wl, seq_lens=None, n_threads=0):
     (configs.HOST.scaled(batch=3, context=8192, top_k=40), [8192, 700, 0], 3),
     (configs.HOST.scaled(batch=2, context=4096, window=0), None, 0),
     (configs.HOST.scaled(batch=2, context=4096, window=0, kv_dtype="fp8"), None, 0),
+    (FP8_WIN, [8192, 300, 0], 0),
+    (FP8_WIN.scaled(block_size=16, window=256), None, 2),
     (configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3), None, 0),
     (configs.HOST.scaled(batch=2, context=4096, head_dim=64, block_size=32, n_q_heads=64), None, 2),
     (configs.HOST.scaled(batch=2, context=4096, n_q_heads=24, top_k=60), None, 0),       # G = 3, k > candidates
@@ -691,6 +708,18 @@ def test_host_layer_pipeline_fp8_odd_layers():
     check_layers_against_oracle(wl, host, pipe.outs)
 
 
+def test_host_layer_pipeline_fp8_window():
+    wl = FP8_WIN.scaled(batch=2)
+    announce("sparsekv_decode_layers, fp8 pool and window buffers, 3 layers, poisoned slots")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(wl, 3)
+    pipe = LayerPipeline(dev)
+    poison(pipe.staging_buffers())
+    pipe.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    check_layers_against_oracle(wl, host, pipe.outs)
+
+
 PRED_WL = configs.HOST.scaled(batch=2, context=8192, n_q_tokens=2, spec_noise=0.3)
 
 
@@ -784,6 +813,22 @@ def test_predicted_layer_pipeline_delayed_copy_stream():
 def test_predicted_layer_pipeline_fp8():
     wl = configs.HOST.scaled(batch=2, context=4096, window=0, kv_dtype="fp8", n_q_tokens=2, spec_noise=0.3)
     announce("sparsekv_decode_layers_predicted, fp8 pool, 3 layers")
+    from sparse_kv_cache_block_amd.step import LayerPipeline
+    host, dev = layer_inputs(wl, 3)
+    plain = LayerPipeline(dev)
+    plain.run(copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    preds = [(o["indices"].clone(), o["n_sel"].clone(), 1) for o in plain.outs]
+    pipe = LayerPipeline(dev)
+    _run_predicted(pipe, preds, torch.cuda.Stream())
+    check_layers_against_oracle(wl, host, pipe.outs)
+    for o, p in zip(pipe.outs, plain.outs):
+        assert torch.equal(o["out"], p["out"]) and torch.equal(o["lse"], p["lse"])
+
+
+def test_predicted_layer_pipeline_fp8_window():
+    wl = FP8_WIN.scaled(batch=2, n_q_tokens=2, spec_noise=0.3)
+    announce("sparsekv_decode_layers_predicted, fp8 pool and window buffers, 3 layers")
     from sparse_kv_cache_block_amd.step import LayerPipeline
     host, dev = layer_inputs(wl, 3)
     plain = LayerPipeline(dev)
