@@ -585,15 +585,66 @@ __device__ __forceinline__ void write_phys(const int32_t* lds_idx, int T, int k_
   }
 }
 
+// The first loads of a scoring workgroup: the G query rows of each token
+// (summed into the group query by score_rows) and the first batch of
+// landmark rows of chunk c.  The batch's rows are clamped to the pair's
+// max_blocks rows, not to its candidates, so its addresses do not wait for
+// the sequence's length; rows past the candidates stay inside the landmark
+// array and are ignored by score_rows.
+template <int UR>
+struct ScoreHead {
+  uint32_t qraw[8];
+  uint4 va[UR];
+};
+
+template <int D, bool LM_F32, bool Q_F32, int NT, int UR>
+__device__ __forceinline__ void score_head(const ScoreParams& p, int c, int g, int b, ScoreHead<UR>& h) {
+  constexpr int NW = NT / kWave;
+  constexpr int ES = LM_F32 ? 4 : 2;
+  constexpr int LPR = D * ES / 16;
+  constexpr int RPW = kWave / LPR;
+  constexpr int RPS = RPW * NW;
+  const int lane = lane_id(), w = wave_id();
+  const int sub = lane % LPR, rw = lane / LPR;
+  const int qi = threadIdx.x;
+  const bool q_owner = qi < p.T * D;
+  {
+    const int t = q_owner ? qi / D : 0, d = q_owner ? qi % D : 0;
+    const int64_t base = ((int64_t)(b * p.T + t) * p.Hq + (int64_t)g * p.G) * D + d;
+    if constexpr (Q_F32) {
+      const uint32_t* qp = static_cast<const uint32_t*>(p.q) + base;
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) h.qraw[hh] = qp[(int64_t)min(hh, p.G - 1) * D];
+    } else {
+      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + base;
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) h.qraw[hh] = qp[(int64_t)min(hh, p.G - 1) * D];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // q loads issue first: waiting on them leaves the batch in flight
+  const char* lm = static_cast<const char*>(p.landmarks) +
+                   ((int64_t)(b * p.Hkv + g) * p.max_blocks) * D * ES + sub * 16;
+  const int row_begin = c * p.rows_per_chunk;
+  const int last_row = max(0, min(p.max_blocks, row_begin + p.rows_per_chunk) - 1);
+#pragma unroll
+  for (int u = 0; u < UR; ++u) {
+    const int r = min(row_begin + u * RPS + w * RPW + rw, last_row);
+    h.va[u] = load_stream16(lm + (int64_t)r * D * ES);
+  }
+}
+
 // Landmark scoring of (b, g) rows of chunk c.  Modes: stand-alone scoring
 // (scores to global, -inf past the candidates); fused with one chunk per
 // (b, g) (scores go straight to the LDS keys for the selection); fused with
 // several chunks (scores are published to the workspace for the chunk that
 // selects).  Returns false when a fused chunk has no rows.  `smem` holds
 // score_lds_bytes().
-// LDS_KEYS: compiled for the fused single-chunk mode only.
+// LDS_KEYS: compiled for the fused single-chunk mode only.  head: the query
+// and first-batch loads score_head issued for the same (c, g, b), or null
+// (then they are issued here).
 template <int D, bool LM_F32, bool Q_F32, int NT, int UR, bool LDS_KEYS = false>
-__device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, int b, uint32_t* smem) {
+__device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, int b, uint32_t* smem,
+                                           const ScoreHead<UR>* head = nullptr) {
   constexpr int NW = NT / kWave;
   constexpr int ES = LM_F32 ? 4 : 2;
   constexpr int LPR = D * ES / 16;      // lanes per landmark row
@@ -652,21 +703,19 @@ __device__ __forceinline__ bool score_rows(const ScoreParams& p, int c, int g, i
   const int qi = threadIdx.x;
   const bool q_owner = qi < T * D;
   uint32_t qraw[8];
-  {
-    const int t = q_owner ? qi / D : 0, d = q_owner ? qi % D : 0;
-    const int64_t base = ((int64_t)(b * T + t) * p.Hq + (int64_t)g * p.G) * D + d;
-    if constexpr (Q_F32) {
-      const uint32_t* qp = static_cast<const uint32_t*>(p.q) + base;
+  if (head) {
 #pragma unroll
-      for (int h = 0; h < 8; ++h) qraw[h] = qp[(int64_t)min(h, p.G - 1) * D];
-    } else {
-      const uint16_t* qp = static_cast<const uint16_t*>(p.q) + base;
+    for (int h = 0; h < 8; ++h) qraw[h] = head->qraw[h];
 #pragma unroll
-      for (int h = 0; h < 8; ++h) qraw[h] = qp[(int64_t)min(h, p.G - 1) * D];
-    }
+    for (int u = 0; u < UR; ++u) va[u] = head->va[u];
+  } else {
+    ScoreHead<UR> own;
+    score_head<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, own);   // always in bounds; ignored without rows
+#pragma unroll
+    for (int h = 0; h < 8; ++h) qraw[h] = own.qraw[h];
+#pragma unroll
+    for (int u = 0; u < UR; ++u) va[u] = own.va[u];
   }
-  __builtin_amdgcn_sched_barrier(0);   // q loads issue first: waiting on them leaves the batch in flight
-  load_batch(va, 0);   // always in bounds (clamped rows); results are ignored without rows
   if (q_owner) {
     float sum = 0.f;
 #pragma unroll

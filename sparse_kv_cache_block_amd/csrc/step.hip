@@ -82,9 +82,15 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
   const int g = a.longest_first ? (int)blockIdx.x : (int)blockIdx.y;
   const int b = a.longest_first ? sequence_of_rank(a.seq_lens, a.B, blockIdx.y) : (int)blockIdx.x;
   const int L = a.seq_lens[b];
+  const int k = s.k_per_seq[b];
+  // the query and the first landmark rows are requested before anything
+  // waits for the sequence's length
+  __builtin_amdgcn_sched_barrier(0);
+  ScoreHead<SKV_PAIR_SCORE_UR> head;
+  score_head<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR>(s, 0, g, b, head);
+  __builtin_amdgcn_sched_barrier(0);
   const int ws = L - a.window > 0 ? L - a.window : 0;
   const int nc = n_candidates(L, a.window, a.blk);
-  const int k = s.k_per_seq[b];
   // the selection returns clamp(min(k, candidates), 0, k_max) blocks
   int nsel = min(k, nc);
   nsel = max(0, min(nsel, a.k_max));
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kPairThreads) void pair_step_kernel(ScoreParams s, 
           __builtin_amdgcn_s_sleep(1);
       },
       [&](auto&& issue_first) {
-        (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem);
+        (void)score_rows<D, false, false, kPairThreads, SKV_PAIR_SCORE_UR, true>(s, 0, g, b, score_smem, &head);
 #pragma unroll
         for (int i = 0; i < kTableRegs; ++i) {
           const int j = (int)threadIdx.x + kPairThreads * i;
