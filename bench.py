@@ -13,7 +13,10 @@ kernel's roofline (algorithmic HBM bytes per launch over its mean launch time
 from HIP events on the launch stream: the single-launch step kernel where the
 step is one launch, else the attention launch timed alone), that rate against
 the streaming-read ceiling of a plain read with the same loads on the same box,
-and the CPU oracle timed on a bounded sample of the same workload.
+and the CPU oracle timed on a bounded sample of the same workload.  After the
+headline workload the same process times the other workloads (--others) and
+adds their step times, per-kernel figures and fractions of peak to the line as
+other_workloads; the headline's own fields are unaffected.
 """
 from __future__ import annotations
 
@@ -510,6 +513,9 @@ def main() -> int:
                     help="only compare co-batched two-token attention with one launch per token and exit")
     ap.add_argument("--layers-predicted", action="store_true",
                     help="only compare the predicted-prefetch layer pipeline with the plain one and exit")
+    ap.add_argument("--others", default="ragged,dual,host,tiny",
+                    help="after the headline workload, time these workloads in the same process and add "
+                         "their figures to the line as other_workloads ('none': skip)")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe, max(1, args.steps))
@@ -532,6 +538,33 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    import gc
+
+    import torch
+
+    line = run_workload(args, args.workload, args.cpu_budget)
+    others = [w for w in args.others.split(",") if w and w != "none" and w != args.workload]
+    if others:
+        line["other_workloads"] = []
+        for name in others:
+            gc.collect()
+            torch.cuda.empty_cache()
+            o = run_workload(args, name, 0.0)
+            keep = ("ms_per_step", "value", "unit", "step_bytes", "step_gbps", "step_frac_of_peak",
+                    "step_us_p10_p50_p90", "launches_per_step", "kernels", "overlap_mean", "host_link")
+            entry = {"workload": name, "config": o["config"]}
+            entry.update({k: o[k] for k in keep if k in o})
+            if o.get("roofline"):
+                entry["roofline_frac"] = o["roofline"]["frac"]
+                entry["frac_of_read_ceiling"] = o["roofline"]["frac_of_read_ceiling"]
+            line["other_workloads"].append(entry)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_workload(args, name: str, cpu_budget: float) -> dict:
+    """Times one workload's decode step (args.warmup untimed, args.steps timed
+    over args.instances input sets) and returns its bench line."""
     import numpy as np
     import torch
 
@@ -540,9 +573,10 @@ def main() -> int:
     from sparse_kv_cache_block_amd.inputs import make_inputs
     from sparse_kv_cache_block_amd.step import DecodeStep, LayerPipeline, to_device_for
 
-    wl = configs.get(args.workload)
+    wl = configs.get(name)
     torch.cuda.set_device(0)
     B.lib()
+    log(f"workload {name}")
 
     # ---- inputs: independent instances generated on the GPU
     steps = []
@@ -550,7 +584,7 @@ def main() -> int:
     for i in range(args.instances):
         t0 = time.perf_counter()
         inp = make_inputs(wl, device="cuda", instance=i)
-        if i == 0 and args.cpu_budget > 0:
+        if i == 0 and cpu_budget > 0:
             host_inputs = inp.to("cpu")
         if wl.pool == "host":
             inp = to_device_for(inp)   # the K/V pool moves to pinned host memory
@@ -725,7 +759,7 @@ def main() -> int:
 
     # ---- CPU oracle on a bounded sample of instance 0
     cpu = None
-    if args.cpu_budget > 0 and host_inputs is not None:
+    if cpu_budget > 0 and host_inputs is not None:
         from oracle import oracle as O
         from tests.common import HostArrays, oracle_problem
         h = HostArrays(host_inputs)
@@ -738,7 +772,7 @@ def main() -> int:
             O.decode_step(pr, h.q, h.landmarks, *h.pools(), h.block_table, h.seq_lens, h.k_per_seq)
             times.append(time.perf_counter() - t0)
             spent = time.perf_counter() - t_start
-            if len(times) >= 100 or (len(times) >= 3 and spent > args.cpu_budget):
+            if len(times) >= 100 or (len(times) >= 3 and spent > cpu_budget):
                 break
         t = statistics.median(times)
         threads = O.max_threads()
@@ -805,8 +839,7 @@ def main() -> int:
                              "h2d_ceiling_gbps": round(ceiling, 2), "frac": round(link_gbps / ceiling, 4),
                              "note": "whole-step time (scoring and attention included) over the "
                                      "gathered K/V bytes; ceiling = 64 MiB pinned hipMemcpyAsync"}
-    print(json.dumps(line), flush=True)
-    return 0
+    return line
 
 
 if __name__ == "__main__":
