@@ -557,7 +557,7 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
   const int NQ = NTOK * G;
   const int64_t pair = (int64_t)b * p.Hkv + g;
   auto out_row = [&](int c) { return ((int64_t)b * NTOK + c / G) * p.Hq + (int64_t)g * G + c % G; };
-  float* part = p.partials + (pair * n_splits + split) * NQ * (D + 2);
+  const Handoff<float> part = p.partials + (pair * n_splits + split) * NQ * (D + 2);
   for (int idx = threadIdx.x; idx < NQ * D; idx += NTH) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
@@ -585,10 +585,10 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
       if (d == 0 && p.lse) p.lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(Ls)) * kLn2;
       continue;
     }
-    publish_f32(part + h * (D + 2) + 2 + d, O);
+    part.put(h * (D + 2) + 2 + d, O);
     if (d == 0) {
-      publish_f32(part + h * (D + 2), M);
-      publish_f32(part + h * (D + 2) + 1, Ls);
+      part.put(h * (D + 2), M);
+      part.put(h * (D + 2) + 1, Ls);
     }
   }
   if (n_splits == 1) return;
@@ -598,7 +598,7 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
   // each thread merges its outputs over the splits online, reading 8 splits'
   // (max, sum, output) per round of loads: one round for up to 8 splits, and
   // no LDS whatever the split count
-  const float* pb = p.partials + pair * n_splits * NQ * (D + 2);
+  const Handoff<float> pb = p.partials + pair * n_splits * NQ * (D + 2);
   for (int idx = threadIdx.x; idx < NQ * D; idx += NTH) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY, Ls = 0.f, acc = 0.f;
@@ -608,10 +608,10 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
         const bool in = s0 + u < n_splits;
-        const float* ps = pb + ((int64_t)(in ? s0 + u : s0) * NQ + h) * (D + 2);
-        mv[u] = fetch_f32(ps);
-        lv[u] = fetch_f32(ps + 1);
-        ov[u] = fetch_f32(ps + 2 + d);
+        const Handoff<float> ps = pb + ((int64_t)(in ? s0 + u : s0) * NQ + h) * (D + 2);
+        mv[u] = ps.get(0);
+        lv[u] = ps.get(1);
+        ov[u] = ps.get(2 + d);
         if (!in) mv[u] = -INFINITY;
       }
       float Mc = M;

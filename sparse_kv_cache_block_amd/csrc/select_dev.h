@@ -837,16 +837,16 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
     const int k_max = p.k_max;
     const int row_begin = c * R;
     const int rows = min(nc, row_begin + R) - row_begin;
-    int32_t* cand = p.cand + ((int64_t)b * T * p.Hkv + g) * p.cand_stride;
+    const Handoff<int32_t> cand = p.cand + ((int64_t)b * T * p.Hkv + g) * p.cand_stride;
     const int64_t cand_t = (int64_t)p.Hkv * p.cand_stride;
     lds_barrier();   // the chunk's keys are in LDS
     const int ns1 = select_lds<NT>(keys + row_begin, p.score_cols, rows, T, k, k_max, lds_idx, sh);
     for (int i = threadIdx.x; i < T * ns1; i += NT) {
       const int t = i / ns1, m = i - t * ns1;
       const int pos = lds_idx[t * k_max + m];
-      int32_t* ct = cand + t * cand_t + (int64_t)c * 2 * k_max;
-      put_i32<true>(ct + m, (int32_t)keys[t * p.score_cols + row_begin + pos]);
-      put_i32<true>(ct + k_max + m, row_begin + pos);
+      const Handoff<int32_t> ct = cand + t * cand_t + (int64_t)c * 2 * k_max;
+      ct.put(m, (int32_t)keys[t * p.score_cols + row_begin + pos]);
+      ct.put(k_max + m, row_begin + pos);
     }
     if (!arrive_last(p.counters + b * p.Hkv + g, (unsigned)nchunks, s_flag)) return false;
     // Level 2, in the last chunk to arrive: every chunk's candidates in chunk
@@ -867,9 +867,9 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
         const int i = i0 + u * NT;
         const int t = i / M, j = i - t * M;
         const int cc = min(j / max(m_full, 1), nchunks - 1);
-        const int32_t* ct = cand + t * cand_t + (int64_t)cc * 2 * k_max + (j - cc * m_full);
-        kv[u] = i < T * M ? fetch_i32(ct) : 0;
-        iv[u] = (ids_lds && i < T * M) ? fetch_i32(ct + k_max) : 0;
+        const Handoff<int32_t> ct = cand + t * cand_t + (int64_t)cc * 2 * k_max + (j - cc * m_full);
+        kv[u] = i < T * M ? ct.get(0) : 0;
+        iv[u] = (ids_lds && i < T * M) ? ct.get(k_max) : 0;
       }
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
@@ -892,7 +892,7 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
           id = ids[t * p.score_cols + pos];
         } else {   // the ids did not fit in LDS: read the selected ones back
           const int cc = min(pos / max(m_full, 1), nchunks - 1);
-          id = fetch_i32(cand + t * cand_t + (int64_t)cc * 2 * k_max + k_max + (pos - cc * m_full));
+          id = cand.get(t * cand_t + (int64_t)cc * 2 * k_max + k_max + (pos - cc * m_full));
         }
       }
       lds_idx[i] = id;

@@ -161,7 +161,9 @@ __device__ __forceinline__ void lds_barrier() {
 // itself: a plain store into the split partials or the candidate rows may
 // still sit in the producer's XCD-private L2 when the last arriver (on
 // another XCD) reads, and would be seen stale.  The s_waitcnt below only makes
-// the atomic stores complete at device scope before the increment.
+// the atomic stores complete at device scope before the increment.  The split
+// partials and the chunks' candidates are held as Handoff buffers
+// (skv_internal.h), which allow no other access.
 __device__ __forceinline__ void publish_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

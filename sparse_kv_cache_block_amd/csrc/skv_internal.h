@@ -28,6 +28,28 @@ skv_status hip_fail(hipError_t e, const char* what);
     if (s_ != SKV_OK) return s_;       \
   } while (0)
 
+// A buffer that the workgroups of one launch hand to each other (split
+// partials, the chunks' candidates).  The XCDs' L2 caches are not coherent
+// with each other, and the hand-off avoids fences (see publish_f32 in
+// skv_device.h), so every value in such a buffer must be written with an
+// agent-scope atomic store and read with an agent-scope atomic load.  The
+// class offers only those two accesses: a plain load or store into the buffer
+// does not compile.
+template <class T>
+class Handoff {
+ public:
+  Handoff() = default;
+  __host__ __device__ explicit Handoff(T* p) : p_(p) {}
+  __host__ __device__ Handoff operator+(int64_t i) const { return Handoff(p_ + i); }
+  __device__ void put(int64_t i, T v) const {
+    __hip_atomic_store(p_ + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ T get(int64_t i) const { return __hip_atomic_load(p_ + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+ private:
+  T* p_ = nullptr;
+};
+
 // ------------------------------------------------------------ scoring / top-k
 struct ScoreParams {
   const void* q;            // [B][T][Hq][d]
@@ -53,7 +75,7 @@ struct ScoreParams {
   // rows, [B][T][Hkv][chunks][2][k_max] (cand_stride = chunks * 2 * k_max);
   // otherwise the chunks publish every score to `scores`
   int two_level;
-  int32_t* cand;
+  Handoff<int32_t> cand;
   int cand_stride;
   int cand_ids_lds;         // 1: the last chunk stages the candidates' ids in LDS (when they fit)
 };
@@ -97,7 +119,7 @@ struct AttnParams {
   // concatenated list (sparse slices, then window slices), n = ceil(items of
   // (b, g) / n_splits) <= items_per_split
   int n_splits, items_per_split;
-  float* partials;          // [B][Hkv][n_splits][tokens * G][d + 2]
+  Handoff<float> partials;  // [B][Hkv][n_splits][tokens * G][d + 2]
   unsigned* counters;       // [B][Hkv]
   float* out;               // [B][Hq][d]; co-batched [B][2][Hq][d]
   float* lse;               // [B][Hq] or null; co-batched [B][2][Hq]

@@ -232,7 +232,7 @@ AttnParams attn_params(const skv_problem& p, const Plan& pl, const void* q, cons
   a.seq_lens = seq_lens;
   a.n_splits = pl.n_splits;
   a.items_per_split = pl.items_per_split;
-  a.partials = reinterpret_cast<float*>(ws + pl.off_partials);
+  a.partials = Handoff<float>(reinterpret_cast<float*>(ws + pl.off_partials));
   a.counters = reinterpret_cast<unsigned*>(ws + pl.off_attn_counters);
   a.out = out;
   a.lse = lse;
@@ -298,7 +298,7 @@ skv_status enqueue_score_select(const skv_problem& p, const Plan& pl, const skv_
   sp.fused_select = 1;
   sp.single_chunk = pl.score_chunks == 1;
   sp.two_level = pl.score_two_level;
-  sp.cand = reinterpret_cast<int32_t*>(ws + pl.off_scores);
+  sp.cand = Handoff<int32_t>(reinterpret_cast<int32_t*>(ws + pl.off_scores));
   sp.cand_stride = pl.score_chunks * 2 * p.k_max;
   sp.cand_ids_lds = score_lds_bytes(sp.T, sp.D, sp.score_cols, sp.k_max, true, false, true) + kScoreStaticLds <=
                     kLdsPerWorkgroup;
