@@ -39,6 +39,8 @@
 // output and lse.
 #pragma once
 
+#include <type_traits>
+
 #include "skv_device.h"
 #include "skv_internal.h"
 
@@ -599,41 +601,67 @@ __device__ __forceinline__ void attend_finish(const AttnParams& p, char* smem, i
   // (max, sum, output) per round of loads: one round for up to 8 splits, and
   // no LDS whatever the split count
   const Handoff<float> pb = p.partials + pair * n_splits * NQ * (D + 2);
-  for (int idx = threadIdx.x; idx < NQ * D; idx += NTH) {
-    const int h = idx / D, d = idx % D;
-    float M = -INFINITY, Ls = 0.f, acc = 0.f;
-    constexpr int SB = 8;
-    for (int s0 = 0; s0 < n_splits; s0 += SB) {
-      float mv[SB], lv[SB], ov[SB];
+  // OU outputs per thread per round, so their loads are in flight together
+  // (two where the outputs outnumber the threads)
+  auto merge = [&](auto ou) {
+    constexpr int OU = decltype(ou)::value;
+    for (int idx0 = threadIdx.x; idx0 < NQ * D; idx0 += OU * NTH) {
+      float M[OU], Ls[OU], acc[OU];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const bool in = s0 + u < n_splits;
-        const Handoff<float> ps = pb + ((int64_t)(in ? s0 + u : s0) * NQ + h) * (D + 2);
-        mv[u] = ps.get(0);
-        lv[u] = ps.get(1);
-        ov[u] = ps.get(2 + d);
-        if (!in) mv[u] = -INFINITY;
+      for (int o = 0; o < OU; ++o) {
+        M[o] = -INFINITY;
+        Ls[o] = acc[o] = 0.f;
       }
-      float Mc = M;
+      constexpr int SB = 8;
+      for (int s0 = 0; s0 < n_splits; s0 += SB) {
+        float mv[OU][SB], lv[OU][SB], ov[OU][SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) Mc = fmaxf(Mc, mv[u]);
-      if (Mc == -INFINITY) continue;
-      const float r = M == -INFINITY ? 0.f : exp2f(M - Mc);
-      Ls *= r;
-      acc *= r;
+        for (int o = 0; o < OU; ++o) {
+          const int idx = idx0 + o * NTH;
+          const int ic = idx < NQ * D ? idx : idx0;
+          const int h = ic / D, d = ic % D;
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        if (mv[u] == -INFINITY) continue;
-        const float f = exp2f(mv[u] - Mc);
-        Ls += f * lv[u];
-        acc += f * ov[u];
+          for (int u = 0; u < SB; ++u) {
+            const bool in = s0 + u < n_splits;
+            const Handoff<float> ps = pb + ((int64_t)(in ? s0 + u : s0) * NQ + h) * (D + 2);
+            mv[o][u] = ps.get(0);
+            lv[o][u] = ps.get(1);
+            ov[o][u] = ps.get(2 + d);
+            if (!in) mv[o][u] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int o = 0; o < OU; ++o) {
+          float Mc = M[o];
+#pragma unroll
+          for (int u = 0; u < SB; ++u) Mc = fmaxf(Mc, mv[o][u]);
+          if (Mc == -INFINITY) continue;
+          const float r = M[o] == -INFINITY ? 0.f : exp2f(M[o] - Mc);
+          Ls[o] *= r;
+          acc[o] *= r;
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            if (mv[o][u] == -INFINITY) continue;
+            const float f = exp2f(mv[o][u] - Mc);
+            Ls[o] += f * lv[o][u];
+            acc[o] += f * ov[o][u];
+          }
+          M[o] = Mc;
+        }
       }
-      M = Mc;
+#pragma unroll
+      for (int o = 0; o < OU; ++o) {
+        const int idx = idx0 + o * NTH;
+        if (idx >= NQ * D) continue;
+        const int h = idx / D, d = idx % D;
+        const int64_t bh = out_row(h);
+        p.out[bh * D + d] = M[o] == -INFINITY ? 0.f : acc[o] / Ls[o];
+        if (d == 0 && p.lse) p.lse[bh] = M[o] == -INFINITY ? -INFINITY : (M[o] + log2f(Ls[o])) * kLn2;
+      }
     }
-    const int64_t bh = out_row(h);
-    p.out[bh * D + d] = M == -INFINITY ? 0.f : acc / Ls;
-    if (d == 0 && p.lse) p.lse[bh] = M == -INFINITY ? -INFINITY : (M + log2f(Ls)) * kLn2;
-  }
+  };
+  if (NQ * D > NTH) merge(std::integral_constant<int, 2>{});
+  else merge(std::integral_constant<int, 1>{});
 }
 
 }  // namespace skv

@@ -49,8 +49,8 @@ size_t select_static_lds_bytes() { return sizeof(TopkShared<kSelThreads>) + size
 
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s) {
   const dim3 grid(chunks, p.Hkv, p.B);
-  const size_t lds = score_lds_bytes(p.T, p.D, p.score_cols, p.k_max, p.fused_select != 0, false,
-                                     p.fused_select && p.two_level && p.cand_ids_lds);
+  const size_t lds = score_lds_bytes(p.T, p.D, p.score_cols, p.k_max, p.fused_select != 0, p.cand_only != 0,
+                                     p.fused_select && p.two_level && p.cand_ids_lds && !p.cand_only);
 #define SKV_SCORE_LAUNCH(D_, LMF, QF) \
   hipLaunchKernelGGL((score_kernel<D_, LMF, QF>), grid, dim3(kSelThreads), lds, s, p)
   const int sel = (p.D == 128 ? 4 : 0) + (p.lm_f32 ? 2 : 0) + (p.q_f32 ? 1 : 0);

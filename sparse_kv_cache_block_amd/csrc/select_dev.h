@@ -839,8 +839,24 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
     const int rows = min(nc, row_begin + R) - row_begin;
     const Handoff<int32_t> cand = p.cand + ((int64_t)b * T * p.Hkv + g) * p.cand_stride;
     const int64_t cand_t = (int64_t)p.Hkv * p.cand_stride;
-    lds_barrier();   // the chunk's keys are in LDS
+    const int32_t* tab = lds_idx + 2 * k_max + 2 * 256;   // cand_only: the chunk's table entries
+    lds_barrier();   // the chunk's keys (and table entries) are in LDS
     const int ns1 = select_lds<NT>(keys + row_begin, p.score_cols, rows, T, k, k_max, lds_idx, sh);
+    if (p.cand_only) {
+      // dense rows: every earlier chunk is full and kept min(k', R) candidates
+      int kk = min(k, nc);
+      kk = max(0, min(kk, k_max));
+      const int at = c * min(kk, R);
+      for (int i = threadIdx.x; i < T * ns1; i += NT) {
+        const int t = i / ns1, m = i - t * ns1;
+        const int pos = lds_idx[t * k_max + m];
+        const Handoff<int32_t> ct = cand + t * cand_t + at + m;
+        ct.put(0, (int32_t)keys[t * p.score_cols + row_begin + pos]);
+        ct.put(p.cand_cols, row_begin + pos);
+        if (t == 0) ct.put(2 * p.cand_cols, tab[pos]);
+      }
+      return false;   // split step: the kernel boundary hands them to the attention launch
+    }
     for (int i = threadIdx.x; i < T * ns1; i += NT) {
       const int t = i / ns1, m = i - t * ns1;
       const int pos = lds_idx[t * k_max + m];
@@ -913,13 +929,38 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
 
 // Scoring of chunk c of (b, g), then (fused) the selection; see score_rows
 // and select_scored.
+// cand_only: the chunk's rows of the block table are loaded before the
+// scoring (up to kChunkTableRegs per thread, the rest after it) and staged in
+// LDS for the candidates' physical blocks.
+constexpr int kChunkTableRegs = 2;
+
 template <int D, bool LM_F32, bool Q_F32, int NT, int UR, bool PUB>
 __device__ __forceinline__ bool score_task(const ScoreParams& p, int c, int g, int b, uint32_t* smem,
                                            TopkShared<NT>& sh, int* s_flag) {
+  const int nc = n_candidates(p.seq_lens[b], p.window, p.blk);
+  const int row_begin = c * p.rows_per_chunk;
+  const int rows = min(nc, row_begin + p.rows_per_chunk) - row_begin;
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_blocks + row_begin;
+  int32_t trow[kChunkTableRegs];
+  if (p.cand_only) {
+#pragma unroll
+    for (int i = 0; i < kChunkTableRegs; ++i) {
+      const int j = (int)threadIdx.x + NT * i;
+      trow[i] = j < rows ? table_row[j] : 0;
+    }
+  }
   if (!score_rows<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, smem)) return false;
   if (!p.fused_select) return false;
-  return select_scored<NT, PUB>(p, c, g, b, n_candidates(p.seq_lens[b], p.window, p.blk), p.k_per_seq[b],
-                                smem, sh, s_flag);
+  if (p.cand_only) {
+    int32_t* tab = reinterpret_cast<int32_t*>(smem + p.T * p.D + p.T * p.score_cols) + 2 * p.k_max + 2 * 256;
+#pragma unroll
+    for (int i = 0; i < kChunkTableRegs; ++i) {
+      const int j = (int)threadIdx.x + NT * i;
+      if (j < rows) tab[j] = trow[i];
+    }
+    for (int j = (int)threadIdx.x + NT * kChunkTableRegs; j < rows; j += NT) tab[j] = table_row[j];
+  }
+  return select_scored<NT, PUB>(p, c, g, b, nc, p.k_per_seq[b], smem, sh, s_flag);
 }
 
 }  // namespace skv

@@ -78,6 +78,13 @@ struct ScoreParams {
   Handoff<int32_t> cand;
   int cand_stride;
   int cand_ids_lds;         // 1: the last chunk stages the candidates' ids in LDS (when they fit)
+  // 1: the chunks publish their candidates and stop there; the attention
+  // launch makes the final selection (split step).  Rows [B][T][Hkv][3]
+  // [cand_cols] (cand_stride = 3 * cand_cols) of keys, ids and physical blocks
+  // (token 0's only), dense in chunk order: chunk c's m-th candidate sits at
+  // c * min(k', rows per chunk) + m, k' the pair's selection size.
+  int cand_only;
+  int cand_cols;
 };
 
 struct TopkParams {
@@ -170,6 +177,11 @@ struct Plan {
   // there are enough pairs to fill the chip)
   int fused_step;
   size_t step_lds;          // dynamic LDS bytes of the step kernel (scoring region)
+  // split step (device pools, few pairs, two-level selection): the scoring
+  // launch publishes the chunks' candidates and the attention launch selects
+  int split_step;
+  int cand_cols;            // split step: chunk candidates per token (chunks x min(k_max, rows))
+  size_t split_lds;         // its dynamic LDS bytes
   // scoring with the fused selection (two-launch, host-pool, hybrid and layer
   // steps): static plus dynamic LDS of its workgroups, and whether that fits
   size_t select_lds;
@@ -212,6 +224,31 @@ size_t step_static_lds_bytes(const skv_problem& p);
 #endif
 constexpr int kStepWaves = SKV_PAIR_WAVES;
 constexpr int kStepMaxItems = kStepWaves * 64;
+// Whether an nw-wave attention workgroup can hold its items as attend_items
+// deals them: up to n_early early items over early_waves waves and up to
+// n_late late items over all nw waves, one descriptor per lane, so at most 64
+// items per wave.
+constexpr bool wave_items_fit(int n_early, int early_waves, int n_late, int nw) {
+  return (n_early + early_waves - 1) / early_waves + (n_late + nw - 1) / nw <= 64;
+}
+// Split step (few pairs): the scoring launch's chunks publish their own
+// candidates, and the second launch (grid n_splits x Hkv x B, 8 waves) makes
+// the final selection in every split and attends the split's share.
+hipError_t launch_split_step(const ScoreParams& s, const AttnParams& a, size_t lds, hipStream_t st);
+// Whether the split step is built for this shape and fits one workgroup's
+// LDS with n_splits splits and cand_cols chunk candidates per token; sets
+// *lds to its dynamic LDS bytes.
+bool split_step_fits(const skv_problem& p, int n_splits, int cand_cols, size_t* lds);
+// The split step's key region (words): T rows of cand_cols keys, and at
+// least the overlap's bitmap of max_blocks bits.
+__host__ __device__ inline int split_step_key_words(int T, int cand_cols, int max_blocks) {
+  const int k = T * cand_cols, bits = (max_blocks + 31) / 32;
+  return k > bits ? k : bits;
+}
+__host__ __device__ inline size_t split_step_lds_bytes(int T, int cand_cols, int k_max, int max_blocks) {
+  return (size_t)4 * (split_step_key_words(T, cand_cols, max_blocks) + (size_t)T * cand_cols + cand_cols +
+                      2 * (size_t)k_max + 2 * 256);
+}
 // LDS of one compute unit on gfx950, the most one workgroup may use.
 constexpr size_t kLdsPerCu = 160 * 1024;
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);

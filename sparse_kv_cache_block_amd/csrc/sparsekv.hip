@@ -160,7 +160,9 @@ Plan make_plan(const skv_problem& p) {
   // single-launch step
   pl.fused_step = 0;
 #ifndef SKV_NO_STEP_KERNEL
-  if (step_kernel_available(p) && pairs >= kStepMinPairs && (p.k_max + nwb) * sub <= kStepMaxItems) {
+  // the window slices go to the waves that do not select, the selected ones to all
+  if (step_kernel_available(p) && pairs >= kStepMinPairs &&
+      wave_items_fit(nwb * sub, kStepWaves - p.n_q_tokens, p.k_max * sub, kStepWaves)) {
     pl.step_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true, true);
     pl.fused_step = pl.step_lds <= kStepMaxScoreLds &&
                     step_static_lds_bytes(p) + pl.step_lds <= kLdsPerCu;
@@ -169,6 +171,18 @@ Plan make_plan(const skv_problem& p) {
   pl.select_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand > 0 ? pl.max_cand : 1, p.k_max, true) +
                   select_static_lds_bytes();
   pl.select_fits = pl.select_lds <= kLdsPerWorkgroup;
+  // split step: with a two-level selection on a device pool, the final select
+  // moves into the attention launch (every split makes it from the chunks'
+  // candidates) instead of running in the scoring launch's last chunk
+  pl.split_step = 0;
+#ifndef SKV_NO_SPLIT_STEP
+  if (!pl.fused_step && pl.score_two_level && pl.select_fits) {
+    pl.cand_cols = pl.score_chunks * std::min(p.k_max, pl.rows_per_chunk);
+    const size_t chunk_lds = score_lds_bytes(p.n_q_tokens, D, pl.max_cand, p.k_max, true, true) +
+                             select_static_lds_bytes();
+    pl.split_step = chunk_lds <= kLdsPerWorkgroup && split_step_fits(p, pl.n_splits, pl.cand_cols, &pl.split_lds);
+  }
+#endif
   size_t off = 0;
   pl.off_score_counters = off;
   off = align256(off + (size_t)pairs * 4);
@@ -177,7 +191,9 @@ Plan make_plan(const skv_problem& p) {
   pl.off_scores = off;
   // stand-alone scores, or a fused selection's per-chunk (key, id) candidates
   const size_t score_words = (size_t)(pl.max_cand > 0 ? pl.max_cand : 1);
-  const size_t cand_words = pl.score_two_level ? (size_t)pl.score_chunks * 2 * p.k_max : 0;
+  const size_t cand_words = !pl.score_two_level ? 0
+                            : pl.split_step ? (size_t)3 * pl.cand_cols
+                                            : (size_t)pl.score_chunks * 2 * p.k_max;
   off = align256(off + (size_t)pairs * p.n_q_tokens * std::max(score_words, cand_words) * 4);
   pl.off_partials = off;
   off = align256(off + (size_t)pairs * part_rows * (D + 2) * 4);
@@ -288,9 +304,10 @@ skv_status check_ws(const Plan& pl, void* ws, size_t bytes) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// Scoring with the in-kernel selection (first half of a decode step).
+// Scoring with the in-kernel selection (first half of a decode step).  With
+// cand_only (split step) the chunks publish their candidates and stop.
 skv_status enqueue_score_select(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
-                                const skv_step_outputs& out, char* ws, hipStream_t s) {
+                                const skv_step_outputs& out, char* ws, hipStream_t s, bool cand_only = false) {
   ScoreParams sp = score_params(p, in.q, in.landmarks, in.seq_lens);
   sp.scores = reinterpret_cast<float*>(ws + pl.off_scores);
   sp.score_cols = pl.max_cand > 0 ? pl.max_cand : 1;
@@ -298,8 +315,10 @@ skv_status enqueue_score_select(const skv_problem& p, const Plan& pl, const skv_
   sp.fused_select = 1;
   sp.single_chunk = pl.score_chunks == 1;
   sp.two_level = pl.score_two_level;
+  sp.cand_only = cand_only;
+  sp.cand_cols = pl.cand_cols;
   sp.cand = Handoff<int32_t>(reinterpret_cast<int32_t*>(ws + pl.off_scores));
-  sp.cand_stride = pl.score_chunks * 2 * p.k_max;
+  sp.cand_stride = cand_only ? 3 * pl.cand_cols : pl.score_chunks * 2 * p.k_max;
   sp.cand_ids_lds = score_lds_bytes(sp.T, sp.D, sp.score_cols, sp.k_max, true, false, true) + kScoreStaticLds <=
                     kLdsPerWorkgroup;
   sp.block_table = in.block_table;
@@ -527,8 +546,23 @@ skv_status enqueue_device_step(const skv_problem& p, const Plan& pl, const skv_s
   AttnParams a;
   SKV_TRY(prepare_attend_paged(p, pl, in, out, ws, &a));
   if (clear_bytes) SKV_TRY_HIP(launch_fill_zero(ws, clear_bytes, s), "workspace clear");
-  SKV_TRY(enqueue_score_select(p, pl, in, out, ws, s));
-  SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+  SKV_TRY(enqueue_score_select(p, pl, in, out, ws, s, pl.split_step != 0));
+  if (!pl.split_step) {
+    SKV_TRY_HIP(launch_attend(a, s), "attention launch");
+    return SKV_OK;
+  }
+  // split step: the final selection and the attention in one launch
+  ScoreParams sp = score_params(p, in.q, in.landmarks, in.seq_lens);
+  sp.score_cols = pl.cand_cols;
+  sp.rows_per_chunk = pl.rows_per_chunk;
+  sp.cand = Handoff<int32_t>(reinterpret_cast<int32_t*>(ws + pl.off_scores));
+  sp.cand_cols = pl.cand_cols;
+  sp.cand_stride = 3 * pl.cand_cols;
+  sp.k_per_seq = in.k_per_seq;
+  sp.indices = out.indices;
+  sp.n_sel = out.n_sel;
+  sp.overlap = p.n_q_tokens == 2 ? out.overlap : nullptr;
+  SKV_TRY_HIP(launch_split_step(sp, a, pl.split_lds, s), "selection + attention launch");
   return SKV_OK;
 }
 

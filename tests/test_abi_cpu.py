@@ -67,9 +67,19 @@ def test_decode_step_launch_count(lib):
     assert B.sparsekv_decode_step_launches(_good_problem()) == 2
     assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, d=64))) == 2
     assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, blk=16))) == 2
-    # more items per (sequence, KV head) than one workgroup's 8 x 64 descriptors
-    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, k_max=495))) == 1
-    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, k_max=496))) == 2
+    # a wave holds at most 64 items (one descriptor per lane): 17 window slices
+    # over the 7 waves that do not select (3 in the first) plus ceil(k_max / 8)
+    # selected ones; k_max 488 fills 64, 489 would need 65
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, k_max=488))) == 1
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, k_max=489))) == 2
+    # two tokens: 6 window waves, still 3 slices in the first
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, T=2, k_max=488))) == 1
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(big, T=2, k_max=489))) == 2
+    # a wider window: 129 slices over 7 waves (19 in the first) leave 45 for
+    # the selected blocks, so k_max 360 still plans one launch and 361 two
+    wide = dict(big, window=4096, max_blocks=1024)
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(wide, k_max=360))) == 1
+    assert B.sparsekv_decode_step_launches(_good_problem(**dict(wide, k_max=361))) == 2
     host = B.make_problem(32, 1, 32, 8, 128, 32, 1024, 32 * 1024, 8 * 32 * 128, 32 * 128, 512, 64,
                           "bf16", "bf16", "bf16", pool_location=B.SKV_POOL_HOST)
     assert B.sparsekv_decode_step_launches(host) == 3

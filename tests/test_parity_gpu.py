@@ -205,6 +205,20 @@ def test_two_level_selection_ragged(wl):
     check_step(wl, seq_lens=[131072, 39584], gen_device="cuda")
 
 
+# The split step (two-level selection on a device pool): every attention split
+# selects from the chunks' candidates.  An empty sequence (no candidates, no
+# window), one whose 6 candidates fit one chunk and are all selected, no window
+# at all, and the dual fp8 shape with NaN-poisoned free blocks and tail rows.
+@pytest.mark.parametrize("wl,lens", [
+    (TWO_LEVEL.scaled(n_q_tokens=2, spec_noise=0.3), [0, 131072]),
+    (TWO_LEVEL, [700, 131072]),
+    (TWO_LEVEL.scaled(window=0), [131072, 39584]),
+    (configs.DUAL.scaled(poison=True), [262144, 100000, 1500, 0]),
+], ids=["empty_sequence", "all_candidates_selected", "no_window", "dual_poisoned_ragged"])
+def test_split_step_edge_cases(wl, lens):
+    check_step(wl, seq_lens=lens, gen_device="cuda")
+
+
 def test_two_level_selection_ties_go_to_lowest_ids():
     def zero_q(inp):
         inp.q.zero_()
@@ -247,6 +261,14 @@ def test_single_launch_bf16(kw, lens):
     args = dict(batch=16, context=4096)
     args.update(kw)
     check_single_launch(configs.LLAMA32K.scaled(**args), seq_lens=lens)
+
+
+def test_single_launch_full_waves():
+    # 17 window slices over the 7 waves that do not select (3 in the first)
+    # and 488 selected blocks over all 8 (61 each): the first window wave
+    # holds 64 items, one per lane, the most a wave takes
+    wl = configs.LLAMA32K.scaled(batch=16, context=32768, top_k=488)
+    check_single_launch(wl)
 
 
 def test_many_blocks_fall_back_to_two_launches():
