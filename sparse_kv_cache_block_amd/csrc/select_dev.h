@@ -639,7 +639,8 @@ __device__ __forceinline__ void score_head(const ScoreParams& p, int c, int g, i
 // several chunks (scores are published to the workspace for the chunk that
 // selects).  Returns false when a fused chunk has no rows.  `smem` holds
 // score_lds_bytes().
-// LDS_KEYS: compiled for the fused single-chunk mode only.  head: the query
+// LDS_KEYS: the keys go to LDS with each token's top-byte histogram (the
+// single-launch step, and the split step's scoring chunks).  head: the query
 // and first-batch loads score_head issued for the same (c, g, b), or null
 // (then they are issued here).
 template <int D, bool LM_F32, bool Q_F32, int NT, int UR, bool LDS_KEYS = false>
@@ -839,24 +840,8 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
     const int rows = min(nc, row_begin + R) - row_begin;
     const Handoff<int32_t> cand = p.cand + ((int64_t)b * T * p.Hkv + g) * p.cand_stride;
     const int64_t cand_t = (int64_t)p.Hkv * p.cand_stride;
-    const int32_t* tab = lds_idx + 2 * k_max + 2 * 256;   // cand_only: the chunk's table entries
-    lds_barrier();   // the chunk's keys (and table entries) are in LDS
+    lds_barrier();   // the chunk's keys are in LDS
     const int ns1 = select_lds<NT>(keys + row_begin, p.score_cols, rows, T, k, k_max, lds_idx, sh);
-    if (p.cand_only) {
-      // dense rows: every earlier chunk is full and kept min(k', R) candidates
-      int kk = min(k, nc);
-      kk = max(0, min(kk, k_max));
-      const int at = c * min(kk, R);
-      for (int i = threadIdx.x; i < T * ns1; i += NT) {
-        const int t = i / ns1, m = i - t * ns1;
-        const int pos = lds_idx[t * k_max + m];
-        const Handoff<int32_t> ct = cand + t * cand_t + at + m;
-        ct.put(0, (int32_t)keys[t * p.score_cols + row_begin + pos]);
-        ct.put(p.cand_cols, row_begin + pos);
-        if (t == 0) ct.put(2 * p.cand_cols, tab[pos]);
-      }
-      return false;   // split step: the kernel boundary hands them to the attention launch
-    }
     for (int i = threadIdx.x; i < T * ns1; i += NT) {
       const int t = i / ns1, m = i - t * ns1;
       const int pos = lds_idx[t * k_max + m];
@@ -929,38 +914,77 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
 
 // Scoring of chunk c of (b, g), then (fused) the selection; see score_rows
 // and select_scored.
-// cand_only: the chunk's rows of the block table are loaded before the
-// scoring (up to kChunkTableRegs per thread, the rest after it) and staged in
-// LDS for the candidates' physical blocks.
+// Split step, scoring launch (cand_only): chunk c of (b, g) scores its rows
+// into LDS, counting each token's top-byte key histogram as it goes; wave t
+// then selects token t's top k' of the chunk alone (no workgroup barrier
+// inside the select), and the chunk publishes (key, id, physical block) of
+// its candidates in dense rows: chunk c's m-th candidate at c * min(k', R) + m,
+// since every earlier chunk is full.  The chunk's rows of the block table are
+// loaded before the scoring (up to kChunkTableRegs per thread, the rest after
+// it) and staged in LDS for the physical blocks.
 constexpr int kChunkTableRegs = 2;
+
+template <int D, bool LM_F32, bool Q_F32, int NT, int UR>
+__device__ __forceinline__ void chunk_candidates(const ScoreParams& p, int c, int g, int b, uint32_t* smem,
+                                                 TopkShared<NT>& sh) {
+  const int T = p.T, R = p.rows_per_chunk, k_max = p.k_max;
+  const int nc = n_candidates(p.seq_lens[b], p.window, p.blk);
+  const int k = p.k_per_seq[b];
+  const int row_begin = c * R;
+  const int rows = min(nc, row_begin + R) - row_begin;
+  const int32_t* table_row = p.block_table + (int64_t)b * p.max_blocks + row_begin;
+  int32_t trow[kChunkTableRegs];
+#pragma unroll
+  for (int i = 0; i < kChunkTableRegs; ++i) {
+    const int j = (int)threadIdx.x + NT * i;
+    trow[i] = j < rows ? table_row[j] : 0;
+  }
+  if (!score_rows<D, LM_F32, Q_F32, NT, UR, true>(p, c, g, b, smem)) return;
+  uint32_t* keys = smem + T * p.D;
+  int32_t* lds_idx = reinterpret_cast<int32_t*>(keys + T * p.score_cols);
+  const uint32_t* hist0 = reinterpret_cast<const uint32_t*>(lds_idx + 2 * k_max);
+  int32_t* tab = lds_idx + 2 * k_max + 2 * 256;
+#pragma unroll
+  for (int i = 0; i < kChunkTableRegs; ++i) {
+    const int j = (int)threadIdx.x + NT * i;
+    if (j < rows) tab[j] = trow[i];
+  }
+  for (int j = (int)threadIdx.x + NT * kChunkTableRegs; j < rows; j += NT) tab[j] = table_row[j];
+  lds_barrier();   // the chunk's keys, their histograms and its table entries are in LDS
+  const int w = wave_id();
+  if (w < T)
+    (void)wave_select(keys + w * p.score_cols + row_begin, rows, k, k_max, lds_idx + w * k_max, sh.hist[w],
+                      hist0 + w * 256);
+  lds_barrier();   // both tokens' chunk selections are in LDS
+  // the chunk keeps clamp(min(k, rows), 0, k_max) candidates; the pair's k'
+  // is clamp(min(k, nc), 0, k_max)
+  int ns1 = min(k, rows), kk = min(k, nc);
+  ns1 = max(0, min(ns1, k_max));
+  kk = max(0, min(kk, k_max));
+  const int at = c * min(kk, R);
+  const Handoff<int32_t> cand = p.cand + ((int64_t)b * T * p.Hkv + g) * p.cand_stride;
+  const int64_t cand_t = (int64_t)p.Hkv * p.cand_stride;
+  for (int i = threadIdx.x; i < T * ns1; i += NT) {
+    const int t = i / ns1, m = i - t * ns1;
+    const int pos = lds_idx[t * k_max + m];
+    const Handoff<int32_t> ct = cand + t * cand_t + at + m;
+    ct.put(0, (int32_t)keys[t * p.score_cols + row_begin + pos]);
+    ct.put(p.cand_cols, row_begin + pos);
+    if (t == 0) ct.put(2 * p.cand_cols, tab[pos]);
+  }
+}
 
 template <int D, bool LM_F32, bool Q_F32, int NT, int UR, bool PUB>
 __device__ __forceinline__ bool score_task(const ScoreParams& p, int c, int g, int b, uint32_t* smem,
                                            TopkShared<NT>& sh, int* s_flag) {
-  const int nc = n_candidates(p.seq_lens[b], p.window, p.blk);
-  const int row_begin = c * p.rows_per_chunk;
-  const int rows = min(nc, row_begin + p.rows_per_chunk) - row_begin;
-  const int32_t* table_row = p.block_table + (int64_t)b * p.max_blocks + row_begin;
-  int32_t trow[kChunkTableRegs];
   if (p.cand_only) {
-#pragma unroll
-    for (int i = 0; i < kChunkTableRegs; ++i) {
-      const int j = (int)threadIdx.x + NT * i;
-      trow[i] = j < rows ? table_row[j] : 0;
-    }
+    chunk_candidates<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, smem, sh);
+    return false;
   }
   if (!score_rows<D, LM_F32, Q_F32, NT, UR>(p, c, g, b, smem)) return false;
   if (!p.fused_select) return false;
-  if (p.cand_only) {
-    int32_t* tab = reinterpret_cast<int32_t*>(smem + p.T * p.D + p.T * p.score_cols) + 2 * p.k_max + 2 * 256;
-#pragma unroll
-    for (int i = 0; i < kChunkTableRegs; ++i) {
-      const int j = (int)threadIdx.x + NT * i;
-      if (j < rows) tab[j] = trow[i];
-    }
-    for (int j = (int)threadIdx.x + NT * kChunkTableRegs; j < rows; j += NT) tab[j] = table_row[j];
-  }
-  return select_scored<NT, PUB>(p, c, g, b, nc, p.k_per_seq[b], smem, sh, s_flag);
+  return select_scored<NT, PUB>(p, c, g, b, n_candidates(p.seq_lens[b], p.window, p.blk), p.k_per_seq[b],
+                                smem, sh, s_flag);
 }
 
 }  // namespace skv

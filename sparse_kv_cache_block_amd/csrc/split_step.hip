@@ -45,6 +45,11 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
   const int L = a.seq_lens[b];
   const int k = s.k_per_seq[b];
   const int T = s.T;
+  const bool writer = split == 0;                  // also selects token 1 and writes the selection
+  const int TS = writer ? T : 1;                   // tokens this workgroup selects
+  const int SC = s.score_cols;
+  const Handoff<int32_t> cand = s.cand + ((int64_t)b * T * s.Hkv + g) * s.cand_stride;
+  const int64_t cand_t = (int64_t)s.Hkv * s.cand_stride;
   const int w = wave_id(), lane = lane_id();
   const int ws = L - a.window > 0 ? L - a.window : 0;
   const int nc = n_candidates(L, a.window, a.blk);
@@ -57,14 +62,11 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
   const int m_full = min(kk, R);
   const int m_last = min(kk, nc - (nchunks - 1) * R);
   const int M = (nchunks - 1) * m_full + m_last;   // candidates per token, chunk after chunk
-  const bool writer = split == 0;                  // also selects token 1 and writes the selection
-  const int TS = writer ? T : 1;                   // tokens this workgroup selects
 
   // dynamic LDS (split_step_lds_bytes): keys [T][score_cols] (later the
   // overlap's bitmap), ids [T][score_cols], token 0's physical blocks
   // [score_cols], the selected positions [2][k_max], top-byte key histograms
   // [2][256]; score_cols holds every chunk's candidates of one token
-  const int SC = s.score_cols;
   uint32_t* keys = sel_smem;
   int32_t* ids = reinterpret_cast<int32_t*>(keys + split_step_key_words(T, SC, s.max_blocks));
   int32_t* phys = ids + T * SC;
@@ -82,10 +84,6 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
   const int sp0 = split * spi, my_sp = max(0, min(spi, nsp - sp0));
 
   const int k_max = s.k_max;
-  const Handoff<int32_t> cand = s.cand + ((int64_t)b * T * s.Hkv + g) * s.cand_stride;
-  const int64_t cand_t = (int64_t)s.Hkv * s.cand_stride;
-  // candidate j of token t: key, id and (token 0) physical block at j of the
-  // token's three dense rows
   auto stash = [&](int t, int j, int32_t key, int32_t id, int32_t ph) {
     keys[t * SC + j] = (uint32_t)key;
     ids[t * SC + j] = id;
@@ -123,24 +121,20 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
           __builtin_amdgcn_s_sleep(1);
       },
       [&](auto&& issue_first) {
-        // The candidates' loads go out first (their addresses need neither the
-        // sequence's length nor its k: slots past the pair's count are read
-        // and dropped), then the window slices', so the wait for the
-        // candidates leaves the slices in flight.
+        // The candidates are stashed before the window slices' loads are
+        // issued: their addresses need neither the sequence's length nor its
+        // k (slots past the pair's count are read and dropped), and the
+        // selection waits for them, not for the slices.
         int32_t kv[kSplitCandRegs], iv[kSplitCandRegs], pv[kSplitCandRegs];
 #pragma unroll
         for (int u = 0; u < kSplitCandRegs; ++u) {
           const int i = (int)threadIdx.x + kSplitThreads * u;
           const int t = i / SC, j = i - t * SC;
-          kv[u] = iv[u] = pv[u] = 0;
-          if (t < TS) {
-            const Handoff<int32_t> cr = cand + t * cand_t + j;
-            kv[u] = cr.get(0);
-            iv[u] = cr.get(SC);
-            if (t == 0) pv[u] = cr.get(2 * SC);
-          }
+          const Handoff<int32_t> cr = t < TS ? cand + t * cand_t + j : cand;
+          kv[u] = cr.get(0);
+          iv[u] = cr.get(SC);
+          pv[u] = cr.get(2 * SC);
         }
-        issue_first();
         lds_barrier();   // the histograms are clear
 #pragma unroll
         for (int u = 0; u < kSplitCandRegs; ++u) {
@@ -154,6 +148,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
           const Handoff<int32_t> cr = cand + t * cand_t + j;
           stash(t, j, cr.get(0), cr.get(SC), t == 0 ? cr.get(2 * SC) : 0);
         }
+        issue_first();
         lds_barrier();   // every candidate and the key histograms are in LDS
       },
       [&] {
