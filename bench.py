@@ -64,6 +64,7 @@ KERNEL_SOURCES = {
     "pair_step_kernel": ("step.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
     "attend_kernel": ("attend.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
     "attend_cobatched_kernel": ("attend.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
+    "split_step_kernel": ("split_step.hip", "attend_dev.h", "select_dev.h", "skv_device.h", "skv_internal.h"),
 }
 
 
@@ -647,10 +648,11 @@ def run_workload(args, name: str, cpu_budget: float) -> dict:
     tokens_per_s = wl.batch * n_layers / (ms_per_step * 1e-3)
 
     # ---- per-kernel figures.  One launch: the step kernel is the step.  Two
-    # launches (device pool): the attention launch is timed alone over the
-    # same instances, and the scoring launch (scoring with the fused top-k) is
-    # the step minus that (consecutive launches leave no gap between them).
-    # Host pool: the gather (pinned pool -> stage, over the host link) and the
+    # launches (device pool): each launch of the step is timed between events
+    # recorded around it (sparsekv_decode_step_launch_times), over the same
+    # instances; the kernels are the ones the plan names (the scoring launch,
+    # then the attention or the split step's selection + attention).  Host
+    # pool: the gather (pinned pool -> stage, over the host link) and the
     # attention of the staged blocks are each timed alone.
     launches = B.sparsekv_decode_step_launches(steps[0].pr)
 
@@ -681,20 +683,17 @@ def run_workload(args, name: str, cpu_budget: float) -> dict:
     sels = [(p.outs[0]["indices"], p.outs[0]["n_sel"]) for p in pipes] if pipes else \
         [(st.indices, st.n_sel) for st in steps]
 
-    def attend_us(staged: bool) -> float:
+    def staged_attend_us() -> float:
+        """The host pool's attention launch alone: staged blocks plus the HBM window."""
         srcs = []
         for i, st in enumerate(steps):
             d = st.inp
-            if staged:
-                pipe = pipes[i]
-                sp = B.kv_source(B.SKV_SRC_STAGED, pipe.k_slots[0], pipe.v_slots[0],
-                                 pipe.k_slot_scales[0] if pipe.k_slot_scales else None,
-                                 pipe.v_slot_scales[0] if pipe.v_slot_scales else None)
-                win = B.kv_source(B.SKV_SRC_WINDOW, d.window_k, d.window_v, d.window_k_scales,
-                                  d.window_v_scales) if wl.window else None
-            else:
-                sp = B.kv_source(B.SKV_SRC_PAGED, d.k_pool, d.v_pool, d.k_scales, d.v_scales, d.block_table)
-                win = sp
+            pipe = pipes[i]
+            sp = B.kv_source(B.SKV_SRC_STAGED, pipe.k_slots[0], pipe.v_slots[0],
+                             pipe.k_slot_scales[0] if pipe.k_slot_scales else None,
+                             pipe.v_slot_scales[0] if pipe.v_slot_scales else None)
+            win = B.kv_source(B.SKV_SRC_WINDOW, d.window_k, d.window_v, d.window_k_scales,
+                              d.window_v_scales) if wl.window else None
             srcs.append((st, sp, win, sels[i]))
 
         def one(k):
@@ -715,15 +714,21 @@ def run_workload(args, name: str, cpu_budget: float) -> dict:
         kernel, k_ms, k_bytes = "pair_step_kernel", ms_per_step, step_bytes
         kernels.append(entry(kernel, k_bytes, k_ms * 1e3))
     elif wl.pool != "host":
-        a_us = attend_us(staged=False)
-        kernel, k_ms, k_bytes = "attend_kernel", a_us * 1e-3, attn_bytes
-        log(f"attention kernel alone: {a_us:.1f} us, {attn_bytes / 1e6:.1f} MB")
-        s_us = ms_per_step * 1e3 - a_us
-        kernels.append(entry("score_kernel", score_bytes, s_us,
-                             note="scoring with the fused top-k; time = step minus the attention launch alone"))
-        kernels.append(entry("attend_kernel", attn_bytes, a_us, note="timed alone over the same instances"))
+        names = [B.sparsekv_decode_step_kernel(steps[0].pr, i) for i in range(launches)]
+        reps = max(1, args.steps // len(steps))
+        per = [B.sparsekv_decode_step_launch_times(st.pr, st.inputs, st.outputs, st.ws, reps) for st in steps]
+        l_us = [statistics.mean(p[i] for p in per) for i in range(launches)]
+        log("launches: " + ", ".join(f"{n} {u:.1f} us" for n, u in zip(names, l_us)))
+        split = names[1] == "split_step_kernel"
+        kernels.append(entry(names[0], score_bytes, l_us[0],
+                             note="scoring with each chunk's own top-k' (its candidates published)" if split
+                             else "scoring with the fused top-k"))
+        kernels.append(entry(names[1], attn_bytes, l_us[1],
+                             note="final top-k from the chunks' candidates, then attention" if split
+                             else "attention of the selected blocks and the window"))
+        kernel, k_ms, k_bytes = names[1], l_us[1] * 1e-3, attn_bytes
     else:
-        a_us = attend_us(staged=True)
+        a_us = staged_attend_us()
         kernels.append(entry("attend_kernel", attn_bytes, a_us,
                              note="staged blocks plus the HBM window, timed alone"))
         link = statistics.mean(configs.host_link_bytes(wl, s.inp.seq_lens.cpu(), s.inp.k_per_seq.cpu())

@@ -197,13 +197,44 @@ skv_status sparsekv_workspace_size(const skv_problem *pr, size_t *bytes);
  * no GPU work): 1 when the whole step runs as a single launch with one
  * workgroup per (sequence, KV head) -- device pool, head_dim 128, bf16
  * queries and landmarks, bf16 or fp8 K/V, blocks of 32 or 64 tokens, at
- * least 128 (sequence, KV head) pairs, and at most 512 32-token slices per
- * pair, counted as (k_max + ceil(W / blk) + 1) * blk / 32 (e.g. k_max <= 495
- * at blocks of 32 and W = 512); 2 for the other device-pool problems (scoring with the
- * selection, then attention); 3 for a host pool (scoring with the
- * selection, gather, attention).  *launches receives the count.
+ * least 128 (sequence, KV head) pairs, and every wave of the pair's 8-wave
+ * workgroup holding at most 64 32-token slices: ceil(w / (8 - T)) window
+ * slices plus ceil(s / 8) selected ones, with w = (ceil(W / blk) + 1) * blk / 32
+ * and s = k_max * blk / 32 (e.g. k_max <= 488 at blocks of 32 and W = 512);
+ * 2 for the other device-pool problems (scoring, then attention); 3 for a
+ * host pool (scoring with the selection, gather, attention).  *launches
+ * receives the count.
  */
 skv_status sparsekv_decode_step_launches(const skv_problem *pr, int32_t *launches);
+
+/*
+ * Name of the kernel that launch `launch` (0-based) of sparsekv_decode_step
+ * runs for a problem (host-only, no GPU work), e.g. to match a profiler's
+ * trace: "pair_step_kernel" (single launch); "score_kernel" then
+ * "split_step_kernel" (few pairs with a two-level selection: the scoring
+ * chunks publish their own top k', and every attention split makes the final
+ * selection from them) or "attend_kernel" (the scoring launch selects);
+ * host pools "score_kernel", "gather_kernel", "attend_kernel".  *name
+ * receives a static string.  SKV_E_SHAPE for a launch outside
+ * [0, sparsekv_decode_step_launches).
+ */
+skv_status sparsekv_decode_step_kernel(const skv_problem *pr, int32_t launch, const char **name);
+
+/*
+ * Per-launch device time of a device-pool decode step, a measurement aid:
+ * enqueues one whole sparsekv_decode_step on `stream`, then each launch of the
+ * step alone, n_steps times back to back (1 <= n_steps <= 4096) between two
+ * events, and writes each launch's mean time in microseconds to
+ * launch_us[0 .. sparsekv_decode_step_launches).  A launch reads what the
+ * launches before it wrote and does not change it, so the repeats compute
+ * the step's own values; a last whole step leaves the outputs as
+ * sparsekv_decode_step would.  Waits for the stream; creates and destroys
+ * its own events.  Host pools: SKV_E_UNSUPPORTED.
+ */
+skv_status sparsekv_decode_step_launch_times(const skv_problem *pr, const skv_step_inputs *in,
+                                             const skv_step_outputs *out, void *workspace,
+                                             size_t workspace_bytes, void *stream, int32_t n_steps,
+                                             float *launch_us);
 skv_status sparsekv_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /*
@@ -311,7 +342,9 @@ skv_status sparsekv_attend_cobatched(const skv_problem *pr, const void *q,
 /*
  * Full decode step.  Device pool: scoring with in-kernel top-k, then
  * attention straight from the paged pool (the gather is fused into the
- * attention's loads; nothing is staged).  Host pool: scoring and top-k on
+ * attention's loads; nothing is staged); with few (sequence, KV head) pairs
+ * and a two-level selection, the final select runs in the attention launch
+ * instead (sparsekv_decode_step_kernel).  Host pool: scoring and top-k on
  * `stream`, the gather from pinned host memory into k_stage/v_stage on
  * `copy_stream` (ordered by events), then attention of the staged blocks plus
  * the HBM window buffers on `stream`.  k_stage/v_stage ([B][Hkv][k_max][blk][d])

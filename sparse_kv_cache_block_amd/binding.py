@@ -28,7 +28,8 @@ EXPORTED = ("sparsekv_status_string", "sparsekv_last_error", "sparsekv_version",
             "sparsekv_topk", "sparsekv_gather", "sparsekv_attend", "sparsekv_decode_step",
             "sparsekv_decode_layers", "sparsekv_decode_step_launches", "sparsekv_gather_correct",
             "sparsekv_attend_cobatched", "sparsekv_decode_step_hybrid", "sparsekv_host_attention",
-            "sparsekv_stream_read", "sparsekv_decode_layers_predicted", "sparsekv_decode_step_noalloc")
+            "sparsekv_stream_read", "sparsekv_decode_layers_predicted", "sparsekv_decode_step_noalloc",
+            "sparsekv_decode_step_kernel", "sparsekv_decode_step_launch_times")
 
 
 class SkvError(RuntimeError):
@@ -103,6 +104,9 @@ def lib() -> C.CDLL:
             "sparsekv_gather_correct": (C.c_int, [P] + [vp] * 7 + [C.c_int32] + [vp] * 6 + [C.c_int32]
                                         + [vp] * 6),
             "sparsekv_decode_step_launches": (C.c_int, [P, C.POINTER(C.c_int32)]),
+            "sparsekv_decode_step_kernel": (C.c_int, [P, C.c_int32, C.POINTER(C.c_char_p)]),
+            "sparsekv_decode_step_launch_times": (C.c_int, [P, C.POINTER(StepInputs), C.POINTER(StepOutputs),
+                                                            vp, sz, vp, C.c_int32, C.POINTER(C.c_float)]),
             "sparsekv_attend": (C.c_int, [P, vp, C.POINTER(KvSource), vp, vp, C.POINTER(KvSource),
                                           vp, vp, vp, vp, sz, vp]),
             "sparsekv_attend_cobatched": (C.c_int, [P, vp, C.POINTER(KvSource), vp, vp,
@@ -175,6 +179,23 @@ def sparsekv_decode_step_launches(pr: Problem) -> int:
     n = C.c_int32(0)
     _check(lib().sparsekv_decode_step_launches(C.byref(pr), C.byref(n)), "sparsekv_decode_step_launches")
     return int(n.value)
+
+
+def sparsekv_decode_step_kernel(pr: Problem, launch: int) -> str:
+    name = C.c_char_p()
+    _check(lib().sparsekv_decode_step_kernel(C.byref(pr), launch, C.byref(name)), "sparsekv_decode_step_kernel")
+    return name.value.decode()
+
+
+def sparsekv_decode_step_launch_times(pr: Problem, inputs: StepInputs, outputs: StepOutputs,
+                                      workspace: torch.Tensor, n_steps: int, stream=None) -> list:
+    n = sparsekv_decode_step_launches(pr)
+    us = (C.c_float * n)()
+    _check(lib().sparsekv_decode_step_launch_times(C.byref(pr), C.byref(inputs), C.byref(outputs),
+                                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _stream(stream), n_steps, us),
+           "sparsekv_decode_step_launch_times")
+    return [float(x) for x in us]
 
 
 def sparsekv_workspace_init(workspace: torch.Tensor, stream=None) -> None:

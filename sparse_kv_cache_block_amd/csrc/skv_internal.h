@@ -199,9 +199,11 @@ skv_status check_device_step(const skv_problem* pr, const skv_step_inputs* in, c
                              Plan* pl);
 // Enqueue a checked device-pool decode step on workspace ws (pl.total_bytes).
 // With clear_bytes > 0, a fill kernel first zeroes ws[0, clear_bytes); every
-// remaining argument check runs before it.
+// remaining argument check runs before it.  only >= 0 (two-launch plans):
+// enqueue launch `only` alone.
 skv_status enqueue_device_step(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
-                               const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes);
+                               const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes,
+                               int only = -1);
 
 hipError_t launch_score(const ScoreParams& p, int chunks, hipStream_t s);
 hipError_t launch_topk(const TopkParams& p, hipStream_t s);

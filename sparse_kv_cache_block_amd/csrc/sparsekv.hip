@@ -518,9 +518,9 @@ struct EventSet {
   ~EventSet() {
     for (int i = 0; i < n; ++i) (void)hipEventDestroy(e[i]);
   }
-  hipError_t make(int count) {
+  hipError_t make(int count, bool timing = false) {
     for (; n < count; ++n) {
-      hipError_t r = hipEventCreateWithFlags(&e[n], hipEventDisableTiming);
+      hipError_t r = hipEventCreateWithFlags(&e[n], timing ? hipEventDefault : hipEventDisableTiming);
       if (r != hipSuccess) return r;
     }
     return hipSuccess;
@@ -541,12 +541,14 @@ skv_status check_device_step(const skv_problem* pr, const skv_step_inputs* in, c
 }
 
 skv_status enqueue_device_step(const skv_problem& p, const Plan& pl, const skv_step_inputs& in,
-                               const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes) {
+                               const skv_step_outputs& out, char* ws, hipStream_t s, size_t clear_bytes,
+                               int only) {
   if (pl.fused_step) return enqueue_step(p, pl, in, out, ws, s, clear_bytes);
   AttnParams a;
   SKV_TRY(prepare_attend_paged(p, pl, in, out, ws, &a));
   if (clear_bytes) SKV_TRY_HIP(launch_fill_zero(ws, clear_bytes, s), "workspace clear");
-  SKV_TRY(enqueue_score_select(p, pl, in, out, ws, s, pl.split_step != 0));
+  if (only != 1) SKV_TRY(enqueue_score_select(p, pl, in, out, ws, s, pl.split_step != 0));
+  if (only == 0) return SKV_OK;
   if (!pl.split_step) {
     SKV_TRY_HIP(launch_attend(a, s), "attention launch");
     return SKV_OK;
@@ -601,6 +603,60 @@ skv_status sparsekv_decode_step_launches(const skv_problem* pr, int32_t* launche
   if (!launches) return fail(SKV_E_NULL, "launches is NULL");
   if (pr->pool_location == SKV_POOL_HOST) *launches = 3;
   else *launches = make_plan(*pr).fused_step ? 1 : 2;
+  return SKV_OK;
+}
+
+skv_status sparsekv_decode_step_kernel(const skv_problem* pr, int32_t launch, const char** name) {
+  SKV_TRY(check_problem(pr));
+  if (!name) return fail(SKV_E_NULL, "name is NULL");
+  static const char* const kHost[] = {"score_kernel", "gather_kernel", "attend_kernel"};
+  static const char* const kFused[] = {"pair_step_kernel"};
+  static const char* const kSplit[] = {"score_kernel", "split_step_kernel"};
+  static const char* const kTwo[] = {"score_kernel", "attend_kernel"};
+  const char* const* names;
+  int n;
+  if (pr->pool_location == SKV_POOL_HOST) {
+    names = kHost;
+    n = 3;
+  } else {
+    const Plan pl = make_plan(*pr);
+    names = pl.fused_step ? kFused : pl.split_step ? kSplit : kTwo;
+    n = pl.fused_step ? 1 : 2;
+  }
+  if (launch < 0 || launch >= n) return fail(SKV_E_SHAPE, "launch %d outside [0, %d)", (int)launch, n);
+  *name = names[launch];
+  return SKV_OK;
+}
+
+skv_status sparsekv_decode_step_launch_times(const skv_problem* pr, const skv_step_inputs* in,
+                                             const skv_step_outputs* out, void* workspace,
+                                             size_t workspace_bytes, void* stream, int32_t n_steps,
+                                             float* launch_us) {
+  Plan pl;
+  SKV_TRY(check_device_step(pr, in, out, &pl));
+  SKV_TRY(check_ws(pl, workspace, workspace_bytes));
+  if (!launch_us) return fail(SKV_E_NULL, "launch_us is NULL");
+  if (n_steps < 1 || n_steps > 4096) return fail(SKV_E_SHAPE, "n_steps %d outside [1, 4096]", (int)n_steps);
+  const int nl = pl.fused_step ? 1 : 2;
+  hipStream_t s = as_stream(stream);
+  char* ws = static_cast<char*>(workspace);
+  EventSet ev;
+  SKV_TRY_HIP(ev.make(2, true), "event create");
+  // one whole step, so every launch finds its inputs; then each launch alone,
+  // n_steps times back to back (a launch does not change what it reads)
+  SKV_TRY(enqueue_device_step(*pr, pl, *in, *out, ws, s, 0));
+  for (int l = 0; l < nl; ++l) {
+    SKV_TRY_HIP(hipEventRecord(ev.e[0], s), "event record");
+    for (int i = 0; i < n_steps; ++i) SKV_TRY(enqueue_device_step(*pr, pl, *in, *out, ws, s, 0, nl == 1 ? -1 : l));
+    SKV_TRY_HIP(hipEventRecord(ev.e[1], s), "event record");
+    SKV_TRY_HIP(hipEventSynchronize(ev.e[1]), "event synchronize");
+    float ms = 0.f;
+    SKV_TRY_HIP(hipEventElapsedTime(&ms, ev.e[0], ev.e[1]), "event time");
+    launch_us[l] = ms * 1e3f / (float)n_steps;
+  }
+  // the outputs end as a whole step leaves them
+  if (nl > 1) SKV_TRY(enqueue_device_step(*pr, pl, *in, *out, ws, s, 0));
+  SKV_TRY_HIP(hipStreamSynchronize(s), "stream synchronize");
   return SKV_OK;
 }
 

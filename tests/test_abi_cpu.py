@@ -85,6 +85,29 @@ def test_decode_step_launch_count(lib):
     assert B.sparsekv_decode_step_launches(host) == 3
 
 
+def test_decode_step_kernel_names(lib):
+    big = dict(B=32, Hq=32, Hkv=8, max_blocks=1024, n_pool_blocks=32 * 1024, window=512, k_max=64)
+    assert B.sparsekv_decode_step_kernel(_good_problem(**big), 0) == "pair_step_kernel"
+    # 4 pairs, 2 x 64 candidates: one chunk per pair, the scoring launch selects
+    small = _good_problem()
+    assert [B.sparsekv_decode_step_kernel(small, i) for i in range(2)] == ["score_kernel", "attend_kernel"]
+    # the dual shape: 32 pairs, 4080 candidates in 8 chunks of 512, k 128: the
+    # chunks keep their own top 128 and the attention launch selects
+    dual = _good_problem(B=4, T=2, Hq=64, Hkv=8, blk=64, max_blocks=4096, n_pool_blocks=4 * 4096,
+                         stride_block=8 * 64 * 128, stride_head=64 * 128, window=1024, k_max=128,
+                         kv_dtype="fp8")
+    assert B.sparsekv_decode_step_launches(dual) == 2
+    assert [B.sparsekv_decode_step_kernel(dual, i) for i in range(2)] == ["score_kernel", "split_step_kernel"]
+    host = B.make_problem(32, 1, 32, 8, 128, 32, 1024, 32 * 1024, 8 * 32 * 128, 32 * 128, 512, 64,
+                          "bf16", "bf16", "bf16", pool_location=B.SKV_POOL_HOST)
+    assert [B.sparsekv_decode_step_kernel(host, i) for i in range(3)] == \
+        ["score_kernel", "gather_kernel", "attend_kernel"]
+    for pr, bad in ((small, 2), (small, -1), (host, 3)):
+        with pytest.raises(B.SkvError) as e:
+            B.sparsekv_decode_step_kernel(pr, bad)
+        assert e.value.status == B.SKV_E_SHAPE
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(Hq=6, Hkv=4), B.SKV_E_SHAPE),
     (dict(T=3), B.SKV_E_SHAPE),

@@ -928,6 +928,28 @@ def test_graph_replays_match_eager(wl):
         assert all(torch.equal(a, b) for a, b in zip(got, ref))
 
 
+@pytest.mark.parametrize("wl,names", [
+    (configs.LLAMA32K.scaled(batch=16, context=4096), ["pair_step_kernel"]),
+    (TWO_LEVEL.scaled(n_q_tokens=2, spec_noise=0.3), ["score_kernel", "split_step_kernel"]),
+    (configs.DUAL.scaled(batch=2, context=8192, top_k=30), ["score_kernel", "attend_kernel"]),
+], ids=["single_launch", "split_step", "two_launches"])
+def test_launch_times_run_the_step(wl, names):
+    """The per-launch timing entry point runs the very step: its outputs equal
+    a plain decode step's bit for bit, and it reports one positive time per
+    launch of the kernels the plan names."""
+    announce(f"launch times {wl.name}")
+    inp, st = run_step(wl, gen_device="cuda")
+    ref = [_np(t).copy() for t in (st.indices, st.n_sel, st.out, st.lse)]
+    for t in (st.indices, st.n_sel, st.out, st.lse):
+        t.fill_(-7)
+    us = B.sparsekv_decode_step_launch_times(st.pr, st.inputs, st.outputs, st.ws, 5)
+    torch.cuda.synchronize()
+    assert [B.sparsekv_decode_step_kernel(st.pr, i) for i in range(len(us))] == names
+    assert len(us) == len(names) and all(u > 0 for u in us)
+    for a, t in zip(ref, (st.indices, st.n_sel, st.out, st.lse)):
+        assert np.array_equal(a, _np(t))
+
+
 def test_concurrent_streams_keep_results():
     # the library keeps no state outside the caller's workspace: two steps with
     # their own workspaces, enqueued on two streams at once, give each one's
