@@ -336,17 +336,25 @@ __device__ __forceinline__ int block_select_two(const uint32_t* keys, int key_st
   return nsel;
 }
 
-// The same selection made by one wave alone, with no workgroup barrier, so
-// the workgroup's other waves can do other work meanwhile.  hist is the
-// wave's own 256-bin LDS histogram; keys, hist0 and lds_out as in
-// block_select.  Keys are read 8 per lane before they are used, so a pass
-// waits for LDS about once per 512 keys; the chosen indices are emitted in
-// ascending order 64 at a time with ballots.  Returns k'.
-__device__ __forceinline__ int wave_select(const uint32_t* keys, int n, int k, int k_max, int32_t* lds_out,
-                                           uint32_t* hist, const uint32_t* hist0 = nullptr) {
+// Where a selection of k' = clamp(min(k, n), 0, k_max) of n keys cuts: every
+// key above thresh is chosen, and the first take_eq keys equal to it in
+// position order (take_all: every key).
+struct SelectCut {
+  uint32_t thresh, take_eq;
+  int kk;
+  int take_all;
+};
+
+// The cut of a selection found by one wave alone (radix passes of 8 bits,
+// with no workgroup barrier, so the workgroup's other waves can do other
+// work meanwhile).  hist is the wave's own 256-bin LDS histogram; keys and
+// hist0 as in block_select.  Keys are read 8 per lane before they are used,
+// so a pass waits for LDS about once per 512 keys.  The passes stop as soon as
+// the boundary digit's bin is taken whole.
+__device__ __forceinline__ SelectCut wave_threshold(const uint32_t* keys, int n, int k, int k_max, uint32_t* hist,
+                                                    const uint32_t* hist0 = nullptr) {
   constexpr int U = 8;  // keys per lane per round of LDS reads
   const int lane = lane_id();
-  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
   int kk = k < n ? k : n;
   if (kk > k_max) kk = k_max;
   if (kk < 0) kk = 0;
@@ -412,6 +420,21 @@ __device__ __forceinline__ int wave_select(const uint32_t* keys, int n, int k, i
     thresh = at_or_above ? prefix - 1u : prefix;
     take_eq = at_or_above ? 0u : remaining;
   }
+  return SelectCut{thresh, take_eq, kk, take_all ? 1 : 0};
+}
+
+// The same selection as block_select made by one wave alone: wave_threshold,
+// then the chosen indices emitted in ascending order 64 at a time with
+// ballots.  Returns k'.
+__device__ __forceinline__ int wave_select(const uint32_t* keys, int n, int k, int k_max, int32_t* lds_out,
+                                           uint32_t* hist, const uint32_t* hist0 = nullptr) {
+  constexpr int U = 8;
+  const int lane = lane_id();
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+  const SelectCut cut = wave_threshold(keys, n, k, k_max, hist, hist0);
+  const int kk = cut.kk;
+  const bool take_all = cut.take_all != 0;
+  const uint32_t thresh = cut.thresh, take_eq = cut.take_eq;
   // emit in ascending index order, 64 keys per ballot: keys above the
   // threshold, and the first take_eq keys equal to it
   if (take_all) {
@@ -444,6 +467,67 @@ __device__ __forceinline__ int wave_select(const uint32_t* keys, int n, int k, i
   for (int m = nsel + lane; m < k_max; m += kWave) lds_out[m] = -1;
   wave_lds_sync();
   return nsel;
+}
+
+// Exclusive prefix sums over NSEG equal segments of a workgroup's NT threads
+// (each segment whole waves; one barrier; the caller alternates `lds_w`
+// between two buffers on consecutive calls).
+template <int NT, int NSEG>
+__device__ __forceinline__ uint32_t segment_exclusive_scan(uint32_t v, uint32_t* lds_w) {
+  constexpr int NW = NT / kWave, WPS = NW / NSEG;
+  static_assert(NW % NSEG == 0, "segments of whole waves");
+  const int lane = lane_id(), w = wave_id();
+  const uint32_t x = wave_inclusive_scan(v);
+  if (lane == kWave - 1) lds_w[w] = x;
+  lds_barrier();
+  const int w0 = (w / WPS) * WPS;
+  uint32_t base = 0;
+#pragma unroll
+  for (int i = 0; i < WPS; ++i) base += (w0 + i < w) ? lds_w[w0 + i] : 0u;
+  return base + x - v;
+}
+
+// The indices the cuts of NTOK tokens choose, emitted in ascending order by
+// all NT threads together, NT / NTOK per token: a token's thread i owns the
+// contiguous positions [i * r, (i + 1) * r), r = ceil(n / (NT / NTOK)); one
+// scan counts the keys equal to the threshold before each thread's run, a
+// second the chosen ones.  Token t's keys are at keys + t * key_stride; it
+// writes out[t * k_max + 0 .. k') and -1 up to k_max; the caller's barrier
+// publishes them.  scan_a and scan_b are two NT / 64-word LDS buffers.
+template <int NT, int NTOK>
+__device__ __forceinline__ void block_emit(const uint32_t* keys, int key_stride, int n, const SelectCut* cuts,
+                                           int k_max, int32_t* out, uint32_t* scan_a, uint32_t* scan_b) {
+  constexpr int NH = NT / NTOK;
+  const int t = (int)threadIdx.x / NH, i = (int)threadIdx.x % NH;
+  const SelectCut cut = cuts[t];
+  const uint32_t* kt = keys + t * key_stride;
+  int32_t* ot = out + t * k_max;
+  const int r = (n + NH - 1) / NH;
+  const int j0 = i * r, j1 = min(n, j0 + r);
+  const bool cutting = !cut.take_all && cut.kk > 0;
+  uint32_t gt = 0, eq = 0;
+  if (cutting) {
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = kt[j];
+      gt += key > cut.thresh ? 1u : 0u;
+      eq += key == cut.thresh ? 1u : 0u;
+    }
+  }
+  // every thread takes part in both scans, whatever its token's cut
+  uint32_t eq_before = segment_exclusive_scan<NT, NTOK>(eq, scan_a);
+  const uint32_t eq_kept = eq_before >= cut.take_eq ? 0u : min(eq, cut.take_eq - eq_before);
+  uint32_t slot = segment_exclusive_scan<NT, NTOK>(gt + eq_kept, scan_b);
+  if (cut.take_all) {
+    for (int j = j0; j < j1; ++j) ot[j] = j;
+  } else if (cutting) {
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = kt[j];
+      const bool is_eq = key == cut.thresh;
+      if (key > cut.thresh || (is_eq && eq_before < cut.take_eq)) ot[slot++] = j;
+      eq_before += is_eq ? 1u : 0u;
+    }
+  }
+  for (int m = cut.kk + i; m < k_max; m += NH) ot[m] = -1;
 }
 
 // |a & b| / |a| for two lists of distinct ids in [0, n_ids) in LDS (1 when a

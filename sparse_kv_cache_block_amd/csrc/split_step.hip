@@ -5,22 +5,25 @@
 // workgroups; each chunk keeps its own top k' and publishes it as (key, id,
 // physical block) rows, then exits (the kernel boundary is the hand-off).
 // Here a pair has n_splits workgroups, and each of them
-//   1. loads the pair's chunk candidates into LDS and, in wave 0 alone, makes
-//      the pair's final selection over them (the same radix select as the
-//      single-launch step; under the selection's total order -- score
+//   1. loads the pair's chunk candidates into LDS and makes the pair's final
+//      selection over them: wave 0 alone finds where the selection cuts (the
+//      radix passes of the single-launch step's select), then all waves emit
+//      the chosen positions in ascending order, each a contiguous run placed
+//      by two block scans.  Under the selection's total order -- score
 //      descending, id ascending -- the pair's top k' lies among its chunks'
-//      top k', so this is the selection over all candidates).  Meanwhile the
-//      other waves attend their share of the recent window, which needs no
-//      index (Beyond abstract: the window is attended densely, the older
-//      entries sparsely per head);
+//      top k', so this is the selection over all candidates.  The loads of
+//      this split's share of the recent window are in flight meanwhile; that
+//      part needs no index (Beyond abstract: the window is attended densely,
+//      the older entries sparsely per head);
 //   2. attends its equal share of the selected blocks, whose ids and physical
 //      blocks are in LDS, so no descriptor waits on a global load;
 //   3. publishes its partial, and the last split of the pair to arrive merges
 //      all of them by log-sum-exp.
 // Every split computes the same selection; split 0 also selects the second
-// query token's blocks (wave 1), and its selecting waves write the ids,
-// counts and the two tokens' overlap (DualDecoder core claim: the speculative
-// token's index is the prediction of the next step's) before they attend.  The arithmetic is that of the
+// query token's blocks (wave 1 finds its cut, half the waves emit each
+// token's positions), and its waves 0 and 1 write the ids, counts and the two
+// tokens' overlap (DualDecoder core claim: the speculative token's index is
+// the prediction of the next step's) before they attend.  The arithmetic is that of the
 // stand-alone kernels (select_dev.h, attend_dev.h).
 #include "attend_dev.h"
 #include "select_dev.h"
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
   extern __shared__ __attribute__((aligned(16))) uint32_t sel_smem[];
   __shared__ TopkShared<kSplitThreads> sh;
   __shared__ int s_flag;
-  __shared__ int s_sel_ready;
+  __shared__ SelectCut s_cut[2];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = a.seq_lens[b];
@@ -73,7 +76,6 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
   int32_t* lds_idx = phys + SC;
   uint32_t* hist0 = reinterpret_cast<uint32_t*>(lds_idx + 2 * s.k_max);
   for (int i = threadIdx.x; i < 2 * 256; i += kSplitThreads) hist0[i] = 0u;
-  if (threadIdx.x == 0) s_sel_ready = 0;
 
   // this split's equal shares of the window slices and of the selected slices
   const int nwin = window_blocks(a, L, ws) * C::SUB;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
 
   attend_items<KV, D, BLK, kSplitWaves, 1, false, kLateStrided>(
       a, smem, b, g, 0, my_win + my_sp, my_win, TS,
-      // window slices, early: taken by the waves that do not select
+      // window slices, early: taken by the waves that do not find a cut
       [&](int item) {
         const int it = win0 + item;
         return describe_window<KV, D, BLK>(a, b, g, it / C::SUB, it % C::SUB, ws);
@@ -116,10 +118,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
         const int pos = lds_idx[it / C::SUB];
         return describe_paged<KV, D, BLK>(ids[pos], phys[pos], it % C::SUB);
       },
-      [&] {
-        while (__hip_atomic_load(&s_sel_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-          __builtin_amdgcn_s_sleep(1);
-      },
+      [] {},   // the selection is in LDS before any wave takes an item (post)
       [&](auto&& issue_first) {
         // The candidates are stashed before the window slices' loads are
         // issued: their addresses need neither the sequence's length nor its
@@ -152,19 +151,24 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
         lds_barrier();   // every candidate and the key histograms are in LDS
       },
       [&] {
-        // wave t selects token t's blocks alone while the other waves attend
-        // the window; wave 0 then releases the waves waiting for its positions
-        if (w >= TS) return;
-        (void)wave_select(keys + w * SC, M, k, k_max, lds_idx + w * k_max, sh.hist[w], hist0 + w * 256);
-        if (w == 0 && lane == 0) __hip_atomic_store(&s_sel_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (!writer) return;
+        // wave t finds where token t's selection cuts, alone (radix passes),
+        // while the window slices' loads are in flight; then every wave
+        // emits its run of the chosen positions
+        if (w < TS) {
+          const SelectCut cut = wave_threshold(keys + w * SC, M, k, k_max, sh.hist[w], hist0 + w * 256);
+          if (lane == 0) s_cut[w] = cut;
+        }
+        lds_barrier();   // the cuts are in LDS
+        if (TS == 2)
+          block_emit<kSplitThreads, 2>(keys, SC, M, s_cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
+        else
+          block_emit<kSplitThreads, 1>(keys, SC, M, s_cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
+        lds_barrier();   // every token's chosen positions are in LDS
+        if (!writer || w >= TS) return;
         write_ids(w);
         if (w != 1) return;
-        // wave 1 (T = 2), once token 0's list exists: |I_0 & I_1| / |I_0|,
-        // through a bitmap of token 1's ids in the key region (both selects
-        // are done with the keys)
-        while (__hip_atomic_load(&s_sel_ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-          __builtin_amdgcn_s_sleep(1);
+        // wave 1 (T = 2): |I_0 & I_1| / |I_0|, through a bitmap of token 1's
+        // ids in the key region (the selection is done with the keys)
         uint32_t* bits = keys;
         const int words = (nc + 31) / 32;
         for (int i = lane; i < words; i += kWave) bits[i] = 0u;
