@@ -64,6 +64,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
   return base + x - v;
 }
 
+// Where a selection of k' = clamp(min(k, n), 0, k_max) of n keys cuts: every
+// key above thresh is chosen, and the first take_eq keys equal to it in
+// position order (take_all: every key).
+struct SelectCut {
+  uint32_t thresh, take_eq;
+  int kk;
+  int take_all;
+};
+
 template <int NT>
 struct TopkShared {
   uint32_t hist[2][256];
@@ -72,6 +81,7 @@ struct TopkShared {
   uint32_t ov_w[NT / kWave];          // list_overlap's per-wave hit counts
   uint32_t digit, above, exact;
   uint32_t digit2[2], above2[2], exact2[2];
+  SelectCut cut[2];                   // the cuts one-wave selects hand to block_emit
 };
 
 template <bool PUB>
@@ -335,15 +345,6 @@ __device__ __forceinline__ int block_select_two(const uint32_t* keys, int key_st
   lds_barrier();
   return nsel;
 }
-
-// Where a selection of k' = clamp(min(k, n), 0, k_max) of n keys cuts: every
-// key above thresh is chosen, and the first take_eq keys equal to it in
-// position order (take_all: every key).
-struct SelectCut {
-  uint32_t thresh, take_eq;
-  int kk;
-  int take_all;
-};
 
 // The cut of a selection found by one wave alone (radix passes of 8 bits,
 // with no workgroup barrier, so the workgroup's other waves can do other
@@ -1000,8 +1001,8 @@ __device__ __forceinline__ bool select_scored(const ScoreParams& p, int c, int g
 // and select_scored.
 // Split step, scoring launch (cand_only): chunk c of (b, g) scores its rows
 // into LDS, counting each token's top-byte key histogram as it goes; wave t
-// then selects token t's top k' of the chunk alone (no workgroup barrier
-// inside the select), and the chunk publishes (key, id, physical block) of
+// then finds where token t's top k' of the chunk cuts, all waves emit the
+// chosen positions, and the chunk publishes (key, id, physical block) of
 // its candidates in dense rows: chunk c's m-th candidate at c * min(k', R) + m,
 // since every earlier chunk is full.  The chunk's rows of the block table are
 // loaded before the scoring (up to kChunkTableRegs per thread, the rest after
@@ -1035,10 +1036,19 @@ __device__ __forceinline__ void chunk_candidates(const ScoreParams& p, int c, in
   }
   for (int j = (int)threadIdx.x + NT * kChunkTableRegs; j < rows; j += NT) tab[j] = table_row[j];
   lds_barrier();   // the chunk's keys, their histograms and its table entries are in LDS
+  // wave t finds where token t's selection cuts, then every wave emits its
+  // run of the chosen positions
   const int w = wave_id();
-  if (w < T)
-    (void)wave_select(keys + w * p.score_cols + row_begin, rows, k, k_max, lds_idx + w * k_max, sh.hist[w],
-                      hist0 + w * 256);
+  if (w < T) {
+    const SelectCut cut = wave_threshold(keys + w * p.score_cols + row_begin, rows, k, k_max, sh.hist[w],
+                                         hist0 + w * 256);
+    if (lane_id() == 0) sh.cut[w] = cut;
+  }
+  lds_barrier();
+  if (T == 2)
+    block_emit<NT, 2>(keys + row_begin, p.score_cols, rows, sh.cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
+  else
+    block_emit<NT, 1>(keys + row_begin, p.score_cols, rows, sh.cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
   lds_barrier();   // both tokens' chunk selections are in LDS
   // the chunk keeps clamp(min(k, rows), 0, k_max) candidates; the pair's k'
   // is clamp(min(k, nc), 0, k_max)

@@ -42,7 +42,6 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
   extern __shared__ __attribute__((aligned(16))) uint32_t sel_smem[];
   __shared__ TopkShared<kSplitThreads> sh;
   __shared__ int s_flag;
-  __shared__ SelectCut s_cut[2];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = a.seq_lens[b];
@@ -156,13 +155,13 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
         // emits its run of the chosen positions
         if (w < TS) {
           const SelectCut cut = wave_threshold(keys + w * SC, M, k, k_max, sh.hist[w], hist0 + w * 256);
-          if (lane == 0) s_cut[w] = cut;
+          if (lane == 0) sh.cut[w] = cut;
         }
         lds_barrier();   // the cuts are in LDS
         if (TS == 2)
-          block_emit<kSplitThreads, 2>(keys, SC, M, s_cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
+          block_emit<kSplitThreads, 2>(keys, SC, M, sh.cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
         else
-          block_emit<kSplitThreads, 1>(keys, SC, M, s_cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
+          block_emit<kSplitThreads, 1>(keys, SC, M, sh.cut, k_max, lds_idx, sh.scan_w[0], sh.scan_w[1]);
         lds_barrier();   // every token's chosen positions are in LDS
         if (!writer || w >= TS) return;
         write_ids(w);
