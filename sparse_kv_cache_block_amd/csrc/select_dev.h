@@ -76,12 +76,14 @@ struct SelectCut {
 template <int NT>
 struct TopkShared {
   uint32_t hist[2][256];
-  uint32_t hist1[2][256];   // the second token's, when two tokens select side by side
+  union {
+    uint32_t hist1[2][256];   // the second token's, when two tokens select side by side (block_select_two)
+    SelectCut cut[2];         // the cuts wave_threshold hands to block_emit (never beside block_select_two)
+  };
   uint32_t scan_w[2][NT / kWave];
   uint32_t ov_w[NT / kWave];          // list_overlap's per-wave hit counts
   uint32_t digit, above, exact;
   uint32_t digit2[2], above2[2], exact2[2];
-  SelectCut cut[2];                   // the cuts one-wave selects hand to block_emit
 };
 
 template <bool PUB>
