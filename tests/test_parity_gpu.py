@@ -899,7 +899,8 @@ def test_alternating_inputs_share_one_workspace():
 
 # ------------------------------------------------------------ graph capture
 @pytest.mark.parametrize("wl", [configs.LLAMA32K.scaled(batch=16, context=4096),          # one launch
-                                configs.DUAL.scaled(batch=2, context=8192, top_k=30)])     # two launches
+                                configs.DUAL.scaled(batch=2, context=8192, top_k=30),      # two launches
+                                TWO_LEVEL.scaled(n_q_tokens=2, spec_noise=0.3)])           # split step
 def test_graph_replays_match_eager(wl):
     # the step enqueues no memset and its kernels return their counters to
     # zero, so a captured step replays exactly; eager work runs between replays

@@ -38,11 +38,14 @@ CASES = [
     configs.LLAMA32K.scaled(batch=2, context=2048, top_k=8),           # smaller: two launches
     configs.DUAL.scaled(batch=2, context=16384, top_k=30),             # fp8, two tokens, split scoring rows
     configs.RAGGED.scaled(batch=40, context=8192),                     # one launch, 320 pairs, longest first
+    configs.LLAMA32K.scaled(batch=2, n_q_heads=8, n_kv_heads=2, context=131072, top_k=16,
+                            n_q_tokens=2, spec_noise=0.3),             # split step: chunks' candidates, then
+                                                                       # selection and attention per split
 ]
 
 
 def test_noalloc_matches_workspace_step_on_consecutive_calls():
-    order = [0, 1, 2, 3, 1, 0]   # each call after one of another size; the second is smaller than the first
+    order = [0, 1, 2, 3, 4, 1, 0]   # each call after one of another size; the second is smaller than the first
     prepared = {}
     for i in order:
         wl = CASES[i]
