@@ -214,7 +214,10 @@ def test_two_level_selection_ragged(wl):
     (TWO_LEVEL, [700, 131072]),
     (TWO_LEVEL.scaled(window=0), [131072, 39584]),
     (configs.DUAL.scaled(poison=True), [262144, 100000, 1500, 0]),
-], ids=["empty_sequence", "all_candidates_selected", "no_window", "dual_poisoned_ragged"])
+    (configs.DUAL.scaled(batch=2, block_size=32), None),                       # fp8, blocks of 32, 16 chunks
+    (TWO_LEVEL.scaled(block_size=64, context=262144), [262144, 150000]),       # bf16, blocks of 64
+], ids=["empty_sequence", "all_candidates_selected", "no_window", "dual_poisoned_ragged", "fp8_block32",
+        "bf16_block64"])
 def test_split_step_edge_cases(wl, lens):
     check_step(wl, seq_lens=lens, gen_device="cuda")
 
