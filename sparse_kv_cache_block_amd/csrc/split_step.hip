@@ -196,8 +196,8 @@ bool split_step_fits(const skv_problem& p, int n_splits, int cand_cols, size_t* 
   const int blk = p.block_size;
   const int sub = blk / attn_item_tokens(p.kv_dtype == SKV_FP8_E4M3FN ? KV_FP8 : KV_BF16, blk);
   const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
-  // split 0's window slices go to the waves that do not select, every
-  // split's selected slices to all of its waves
+  // a split's window slices go to the waves that do not find a cut (8 - T in
+  // split 0), its selected slices to all of its waves
   const int win_per_split = (nwb * sub + n_splits - 1) / n_splits;
   const int sel_per_split = (p.k_max * sub + n_splits - 1) / n_splits;
   if (!wave_items_fit(win_per_split, kSplitWaves - p.n_q_tokens, sel_per_split, kSplitWaves)) return false;
