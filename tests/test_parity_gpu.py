@@ -241,6 +241,41 @@ def test_two_level_selection_shapes(wl):
     check_step(wl, gen_device="cuda")
 
 
+def _random_split_shapes(n, seed=11):
+    """Seeded random few-pair shapes whose device step takes the split step."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        wl = configs.LLAMA32K.scaled(
+            name=f"split{len(out)}", batch=int(rng.integers(1, 4)), n_kv_heads=hkv,
+            n_q_heads=hkv * int(rng.choice([1, 2, 4, 8])), block_size=int(rng.choice([32, 64])),
+            context=int(rng.choice([98304, 131072, 196608])), top_k=int(rng.integers(1, 200)),
+            window=int(rng.choice([0, 64, 256, 1024])), n_q_tokens=int(rng.choice([1, 2])),
+            kv_dtype=str(rng.choice(["bf16", "fp8"])), spec_noise=0.3, outlier_channels=0,
+            seed=int(rng.integers(0, 1 << 16)))
+        if wl.batch * wl.n_kv_heads >= 128 or wl.top_k > wl.max_blocks:
+            continue
+        pr = B.make_problem(wl.batch, wl.n_q_tokens, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.block_size,
+                            wl.max_blocks, wl.batch * wl.max_blocks, wl.n_kv_heads * wl.block_size * wl.head_dim,
+                            wl.block_size * wl.head_dim, wl.window, wl.top_k, wl.q_dtype, wl.kv_dtype,
+                            wl.landmark_dtype)
+        if B.sparsekv_decode_step_kernel(pr, 1) != "split_step_kernel":
+            continue
+        lens = [int(x) for x in rng.integers(0, wl.context + 1, size=wl.batch)]
+        lens[0] = wl.context
+        out.append((wl, lens))
+    return out
+
+
+@pytest.mark.parametrize("wl,lens", _random_split_shapes(8), ids=lambda v: getattr(v, "name", None))
+def test_split_step_random_shapes(wl, lens):
+    """Seeded random few-pair shapes (batch, heads, group size, block size,
+    context, k, window, tokens, K/V type, lengths) that the plan sends to the
+    split step, against the oracle."""
+    check_step(wl, seq_lens=lens, gen_device="cuda")
+
+
 # ------------------------------------------------ single-launch step (>= 128 pairs)
 # 16 sequences x 8 KV heads: decode_step runs as one launch, one workgroup per pair
 MIXED16 = [4096, 1000, 513, 37, 0, 1, 512, 513, 4000, 2048, 3333, 4095, 64, 700, 2500, 4096]
