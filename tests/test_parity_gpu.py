@@ -216,8 +216,9 @@ def test_two_level_selection_ragged(wl):
     (configs.DUAL.scaled(poison=True), [262144, 100000, 1500, 0]),
     (configs.DUAL.scaled(batch=2, block_size=32), None),                       # fp8, blocks of 32, 16 chunks
     (TWO_LEVEL.scaled(block_size=64, context=262144), [262144, 150000]),       # bf16, blocks of 64
+    (configs.RAGGED.scaled(batch=4, context=131072), None),                    # k = 2% of each sequence's blocks
 ], ids=["empty_sequence", "all_candidates_selected", "no_window", "dual_poisoned_ragged", "fp8_block32",
-        "bf16_block64"])
+        "bf16_block64", "ragged_k"])
 def test_split_step_edge_cases(wl, lens):
     check_step(wl, seq_lens=lens, gen_device="cuda")
 
