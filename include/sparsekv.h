@@ -45,9 +45,13 @@
  *   overlap    [B][Hkv] fp32 = |I_real & I_spec| / |I_real| (T == 2)
  *
  * Ownership and execution: the caller owns every buffer (device memory, or
- * pinned host memory for a host pool).  The library never allocates, frees or
- * synchronises; all work is enqueued on the given HIP stream (NULL = default
- * stream) and is asynchronous.  Keep buffers alive until it completes.
+ * pinned host memory for a host pool).  The library allocates no memory (the
+ * host-pool paths create HIP events to order their two streams); all work is
+ * enqueued on the given HIP stream (NULL = default stream) and is
+ * asynchronous, except where an entry point says it waits: the hybrid step
+ * (its CPU part needs the selection) and the measurement aid
+ * sparsekv_decode_step_launch_times.  Keep buffers alive until the work
+ * completes.
  *
  * Errors: every argument is checked on the host before any launch; a bad
  * argument returns a non-zero status and launches nothing.  Unsupported
