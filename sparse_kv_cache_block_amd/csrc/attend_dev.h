@@ -53,7 +53,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 template <int KV, int D, int BLK>
 struct AttnCfg {
   static constexpr int ES = KV == KV_F32 ? 4 : (KV == KV_BF16 ? 2 : 1);
-  static constexpr int TB = attn_item_tokens(KV, BLK);  // tokens per item
+  static constexpr int TB = attn_item_tokens(KV, BLK, D);  // tokens per item
   static constexpr int SUB = BLK / TB;                   // items per block
   static constexpr int NT = TB / 16;                     // QK tiles per item
   static constexpr int DT = D / 16;                      // PV output tiles

@@ -17,11 +17,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 enum KvKind { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 // Tokens per attention item (one slice of a block): 32, or the whole block
-// when it is shorter.  (64-token fp8 items, the same 16 KB of K and V as a
-// bf16 item, measured slower on the 262k dual-query workload: its waves hold
-// two or three items each and are latency bound, so the item size is kept.)
-__host__ __device__ constexpr int attn_item_tokens(int kv, int blk) {
-  return (void)kv, blk < 32 ? blk : 32;
+// when it is shorter; 16 for fp32 K/V with d = 128, whose 32-token item
+// (32 KB of K and V in registers) would not fit a wave's registers.  (64-token
+// fp8 items, the same 16 KB of K and V as a bf16 item, measured slower on the
+// 262k dual-query workload: its waves hold two or three items each and are
+// latency bound, so the item size is kept.)
+__host__ __device__ constexpr int attn_item_tokens(int kv, int blk, int d) {
+  return blk < 16 ? blk : (kv == KV_F32 && d == 128) ? 16 : (blk < 32 ? blk : 32);
 }
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;

@@ -136,7 +136,7 @@ Plan make_plan(const skv_problem& p) {
                            kTwoLevelMinSaving;
   // attention: items (32-token slices) of the sparse + window list per split,
   // aiming at about three resident workgroups per compute unit
-  const int sub = blk / attn_item_tokens(kv_kind(p.kv_dtype), blk);
+  const int sub = blk / attn_item_tokens(kv_kind(p.kv_dtype), blk, p.head_dim);
   const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
   const int total_items = (p.k_max + nwb) * sub;
   int ips = (int)(((int64_t)pairs * total_items + kAttnTargetWorkgroups - 1) / kAttnTargetWorkgroups);

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_step_kernel(ScoreParams s
 bool split_step_fits(const skv_problem& p, int n_splits, int cand_cols, size_t* lds) {
   if (!step_kernel_available(p)) return false;
   const int blk = p.block_size;
-  const int sub = blk / attn_item_tokens(p.kv_dtype == SKV_FP8_E4M3FN ? KV_FP8 : KV_BF16, blk);
+  const int sub = blk / attn_item_tokens(p.kv_dtype == SKV_FP8_E4M3FN ? KV_FP8 : KV_BF16, blk, p.head_dim);
   const int nwb = p.window == 0 ? 0 : (p.window + blk - 1) / blk + 1;
   // a split's window slices go to the waves that do not find a cut (8 - T in
   // split 0), its selected slices to all of its waves

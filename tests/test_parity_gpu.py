@@ -141,8 +141,10 @@ def test_fp8_variants(kw):
     check_step(configs.DUAL.scaled(batch=2, context=4096, window=256, top_k=20, **kw))
 
 
-def test_fp32_variants():
-    check_step(configs.TINY.scaled(batch=2, head_dim=128, block_size=32), seq_lens=[4096, 777])
+@pytest.mark.parametrize("blk", [32, 64])
+def test_fp32_variants(blk):
+    # fp32 K/V at d = 128 attends 16-token slices (a 32-token one would not fit a wave's registers)
+    check_step(configs.TINY.scaled(batch=2, head_dim=128, block_size=blk), seq_lens=[4096, 777])
 
 
 def test_zero_query_ties_go_to_lowest_ids():
@@ -500,6 +502,7 @@ def check_cobatched(wl, seq_lens=None, mutate=None):
     (configs.LLAMA32K.scaled(batch=2, context=3000, n_q_tokens=2, spec_noise=0.3, block_size=16,
                              head_dim=64, window=0), [3000, 1]),
     (configs.TINY.scaled(n_q_tokens=2, spec_noise=0.3), None),                      # fp32
+    (configs.TINY.scaled(n_q_tokens=2, spec_noise=0.3, head_dim=128, block_size=32), None),  # fp32, 16-token slices
 ])
 def test_cobatched_attention(wl, lens):
     check_cobatched(wl, seq_lens=lens)
