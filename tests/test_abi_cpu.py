@@ -280,6 +280,24 @@ def _decode_step(lib, pr, ws_bytes=16):
                                     None, None)
 
 
+def test_launch_times_checks_before_any_gpu_work(lib):
+    """The timing aid rejects its bad arguments on the host (no GPU here)."""
+    ins, outs = _step_args()
+    pr = _good_problem()
+    ws = B.sparsekv_workspace_size(pr)
+    us = (C.c_float * 2)()
+
+    def call(p, n_steps=5, out=us, ws_bytes=ws):
+        return lib.sparsekv_decode_step_launch_times(C.byref(p), C.byref(ins), C.byref(outs), D, ws_bytes,
+                                                     None, n_steps, out)
+    assert call(pr, out=None) == B.SKV_E_NULL
+    assert call(pr, n_steps=0) == B.SKV_E_SHAPE and call(pr, n_steps=4097) == B.SKV_E_SHAPE
+    assert call(pr, ws_bytes=16) == B.SKV_E_WORKSPACE
+    host = B.make_problem(2, 1, 8, 2, 128, 32, 64, 128, 2 * 32 * 128, 32 * 128, 64, 8, "bf16", "bf16", "bf16",
+                          pool_location=B.SKV_POOL_HOST)
+    assert call(host) == B.SKV_E_UNSUPPORTED
+
+
 def _limit_problem(T, k_max, B_=1, **kw):
     # 16384 blocks of 64 tokens, window 256: 16380 candidates per sequence
     base = dict(B=B_, T=T, Hq=32, Hkv=8, blk=64, max_blocks=16384, n_pool_blocks=16384 * B_,
